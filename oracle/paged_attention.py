@@ -1,0 +1,252 @@
+"""CPU oracle for attention over a paged KV cache (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke entry point and
+the benchmark's CPU-baseline leg may import this module.  It shares no code
+with the HIP library and imports nothing from it.
+
+What it computes, and where that is defined
+-------------------------------------------
+* Attention is ``softmax(q K^T * scale) V`` evaluated exactly (up to fp64
+  rounding) on the values stored in the cache.  The pages name the operation
+  and its pieces: paged attention over 16-token pages (TinyLoop "Current
+  Status", table "KV cache modes", row "Paged attention"), cached decode
+  (same page, table "Core inference", row "Generation"), GQA with fewer KV
+  heads than query heads (same page, table "Model architecture support", row
+  "GQA"), chunked prefill (same table, row "Chunked prefill"; Tiny-LLM
+  "Project Status", the supported-features list and the release paragraph
+  naming the chunked-prefill SDPA path).
+* KV storage dtypes fp32 / bf16 / fp16 / int8: Tiny-LLM "Project Status"
+  (dtype-contract paragraph: separate compute and KV-cache dtypes, a BF16 KV
+  cache with its own paged kernel), mini-llm README (hardware table: FP16 KV
+  cache), TinyLoop "Current Status" (table "KV cache modes", row "INT8 KV
+  cache").
+
+Readings taken where the pages are silent (each is also listed in the design
+notes):
+* Layout: K pages are ``[num_pages, Hkv, 16, d]``; V pages are stored with
+  the token index innermost, ``[num_pages, Hkv, d, 16]``; int8 scales are
+  ``[num_pages, Hkv, 16]`` float32 for K and for V.
+* GQA map: query head ``h`` reads KV head ``h // (Hq // Hkv)``.
+* Decode: ``context_lens[b]`` counts the query token itself (its K/V are in
+  the cache already); the query attends to positions ``[0, ctx_b)``.
+  ``ctx_b == 0`` yields zeros.
+* Prefill: the chunk's K/V are in the cache; ``context_lens[b] = P_b + C_b``
+  where ``C_b`` is the chunk length from ``cu_q_lens``; chunk row ``i`` sits at
+  absolute position ``P_b + i`` and attends to ``[0, P_b + i]`` (causal,
+  aligned at the bottom right).
+* int8: symmetric absmax per (token, KV head): ``scale = absmax / 127`` in
+  IEEE fp32, ``code = clip(rint(x / scale), -127, 127)`` with ties to even;
+  an all-zero vector gets scale 0 and codes 0.  The pages say only "INT8 KV",
+  so this convention is parity unpinned beyond its own definition; the
+  pinned properties are the rounding bound, the +-127 code at the absmax and
+  sign symmetry.
+* bf16 from fp32: round to nearest even on the bit pattern; NaN stays NaN.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE_SIZE = 16
+DTYPES = ("f32", "bf16", "f16", "i8")
+
+
+# ---------------------------------------------------------------- conversions
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns the
+    16-bit patterns as uint16."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    nan = np.isnan(x)
+    rounded = np.where(nan, (u >> 16) | 0x0040, rounded)
+    return (rounded & 0xFFFF).astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact: bf16 -> fp32 is a 16-bit shift)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_to_f16(x) -> np.ndarray:
+    """fp32 -> fp16, nearest-even with subnormals (numpy's IEEE cast)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16)
+
+
+def quantize_int8(x):
+    """Symmetric absmax int8 over the last axis, all arithmetic in fp32.
+
+    Returns (codes int8 [..., d], scale float32 [...])."""
+    x = np.asarray(x, dtype=np.float32)
+    absmax = np.max(np.abs(x), axis=-1)
+    scale = (absmax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    ratio = (x / safe[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(ratio), -127, 127)
+    codes = np.where((scale > 0)[..., None], codes, 0).astype(np.int8)
+    return codes, scale
+
+
+def storage_from_f32(x, dtype: str):
+    """Convert float32 values to the cache's storage representation.
+
+    f32 -> float32, bf16 -> uint16 bit patterns, f16 -> float16,
+    i8 -> (int8 codes, float32 scales over the last axis)."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).copy()
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return f32_to_f16(x)
+    if dtype == "i8":
+        return quantize_int8(x)
+    raise ValueError(dtype)
+
+
+def upcast(stored, dtype: str, scales=None) -> np.ndarray:
+    """Stored cache values -> float64, exactly."""
+    if dtype == "f32":
+        return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(stored)
+    if dtype == "f16":
+        return np.asarray(stored, dtype=np.float16).astype(np.float64)
+    if dtype == "i8":
+        return np.asarray(stored, dtype=np.int8).astype(np.float64) * \
+            np.asarray(scales, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------- cache
+_STORE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "i8": np.int8}
+
+
+class PagedCache:
+    """Host copy of a paged KV pool in its storage representation."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, dtype: str):
+        if dtype not in DTYPES:
+            raise ValueError(dtype)
+        self.num_pages, self.num_kv_heads, self.head_dim, self.dtype = \
+            num_pages, num_kv_heads, head_dim, dtype
+        st = _STORE[dtype]
+        self.k = np.zeros((num_pages, num_kv_heads, PAGE_SIZE, head_dim), dtype=st)
+        self.v = np.zeros((num_pages, num_kv_heads, head_dim, PAGE_SIZE), dtype=st)
+        if dtype == "i8":
+            self.k_scales = np.zeros((num_pages, num_kv_heads, PAGE_SIZE), np.float32)
+            self.v_scales = np.zeros((num_pages, num_kv_heads, PAGE_SIZE), np.float32)
+        else:
+            self.k_scales = self.v_scales = None
+
+    def copy(self) -> "PagedCache":
+        c = PagedCache.__new__(PagedCache)
+        c.num_pages, c.num_kv_heads, c.head_dim, c.dtype = \
+            self.num_pages, self.num_kv_heads, self.head_dim, self.dtype
+        c.k, c.v = self.k.copy(), self.v.copy()
+        c.k_scales = None if self.k_scales is None else self.k_scales.copy()
+        c.v_scales = None if self.v_scales is None else self.v_scales.copy()
+        return c
+
+
+def ref_append(cache: PagedCache, k_new, v_new, slot_mapping) -> None:
+    """Write new tokens into the pool through the slot mapping (in place).
+
+    ``k_new``/``v_new`` are [T, Hkv, d] float32 (the exact values of whatever
+    dtype the caller holds them in).  Token ``j`` with ``slot >= 0`` goes to
+    page ``slot // 16``, offset ``slot % 16``; negative slots are skipped."""
+    k_new = np.asarray(k_new, dtype=np.float32)
+    v_new = np.asarray(v_new, dtype=np.float32)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = slots >= 0
+    slots, k_new, v_new = slots[keep], k_new[keep], v_new[keep]
+    page, off = slots // PAGE_SIZE, slots % PAGE_SIZE
+    if cache.dtype == "i8":
+        kq, ks = quantize_int8(k_new)
+        vq, vs = quantize_int8(v_new)
+        cache.k[page, :, off, :] = kq
+        cache.v[page, :, :, off] = vq
+        cache.k_scales[page, :, off] = ks
+        cache.v_scales[page, :, off] = vs
+    else:
+        cache.k[page, :, off, :] = storage_from_f32(k_new, cache.dtype)
+        cache.v[page, :, :, off] = storage_from_f32(v_new, cache.dtype)
+
+
+def gather_sequence(cache: PagedCache, block_row, n: int):
+    """Contiguous float64 K, V [n, Hkv, d] of one sequence's first n tokens."""
+    t = np.arange(n)
+    page = np.asarray(block_row, dtype=np.int64)[t // PAGE_SIZE]
+    off = t % PAGE_SIZE
+    ks = None if cache.k_scales is None else cache.k_scales[page, :, off][..., None]
+    vs = None if cache.v_scales is None else cache.v_scales[page, :, off][..., None]
+    K = upcast(cache.k[page, :, off, :], cache.dtype, ks)
+    V = upcast(cache.v[page, :, :, off], cache.dtype, vs)
+    return K, V
+
+
+# ---------------------------------------------------------------- attention
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def ref_decode(q, cache: PagedCache, block_tables, context_lens, scale,
+               num_q_heads: int) -> np.ndarray:
+    """Batched decode: out[b, h] = softmax(scale * K_b q_bh) V_b over [0, ctx_b).
+
+    q: [B, Hq, d] (any float dtype, widened exactly).  Returns float64."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    G = Hq // cache.num_kv_heads
+    sc = float(np.float32(scale))
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    for b in range(B):
+        n = int(context_lens[b])
+        if n == 0:
+            continue
+        K, V = gather_sequence(cache, block_tables[b], n)
+        for h in range(Hq):
+            g = h // G
+            s = sc * (K[:, g, :] @ q[b, h])
+            w = _softmax_rows(s)
+            out[b, h] = w @ V[:, g, :]
+    return out
+
+
+def ref_prefill_chunk(q, cache: PagedCache, block_tables, context_lens, cu_q_lens,
+                      scale) -> np.ndarray:
+    """Chunked causal prefill.  q: [T, Hq, d]; sequence b's chunk is rows
+    cu_q_lens[b]:cu_q_lens[b+1]; row i of it attends to [0, P_b + i] with
+    P_b = context_lens[b] - C_b.  Returns float64 [T, Hq, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    T, Hq, d = q.shape
+    G = Hq // cache.num_kv_heads
+    sc = float(np.float32(scale))
+    out = np.zeros((T, Hq, d), dtype=np.float64)
+    for b in range(len(context_lens)):
+        r0, r1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+        C, n = r1 - r0, int(context_lens[b])
+        if C == 0:
+            continue
+        P = n - C
+        if P < 0:
+            raise ValueError("context shorter than its query chunk")
+        K, V = gather_sequence(cache, block_tables[b], n)
+        keypos = np.arange(n)[None, :]
+        rowpos = P + np.arange(C)[:, None]
+        for h in range(Hq):
+            g = h // G
+            s = sc * (q[r0:r1, h, :] @ K[:, g, :].T)
+            s = np.where(keypos <= rowpos, s, -np.inf)
+            out[r0:r1, h] = _softmax_rows(s) @ V[:, g, :]
+    return out
+
+
+# ---------------------------------------------------------------- comparison
+def max_abs_err(gpu_out, ref) -> float:
+    """max |gpu - ref| over all elements; NaN/inf anywhere -> inf."""
+    g = np.asarray(gpu_out, dtype=np.float64)
+    if not np.all(np.isfinite(g)):
+        return float("inf")
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0

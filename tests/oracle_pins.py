@@ -1,0 +1,370 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` takes an oracle module ``O`` and raises AssertionError (or any
+exception) when the oracle violates what the pages and the mathematics fix:
+brute force with ``math.fsum`` on tiny inputs, torch's fp64 SDPA on the CPU,
+closed forms, invariants, the causal structure, library cross-checks of the
+conversions and hand-derived golden values.  The same pins run against the
+real oracle (they must all pass) and against deliberately broken copies of it
+(each copy must fail at least one), so a plausible slip in the oracle cannot
+hide.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from workloads import custom_workload
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+PS = 16
+
+
+# ------------------------------------------------------------------ helpers
+def _seq(w, arr, b):
+    return arr[int(w.token_offsets[b]):int(w.token_offsets[b + 1])]
+
+
+def write_paged_f32(O, seqs_k, seqs_v, block_tables, num_pages, hkv, d):
+    """Lay dense per-sequence K/V ([n, Hkv, d] each) into an fp32 pool with
+    explicit loops over the layout definition: K[page, g, off, i] and
+    V[page, g, i, off] for token t at page block_tables[b][t // 16],
+    offset t % 16."""
+    cache = O.PagedCache(num_pages, hkv, d, "f32")
+    for b, (ks, vs) in enumerate(zip(seqs_k, seqs_v)):
+        for t in range(len(ks)):
+            page, off = int(block_tables[b][t // PS]), t % PS
+            for g in range(hkv):
+                for i in range(d):
+                    cache.k[page, g, off, i] = ks[t][g][i]
+                    cache.v[page, g, i, off] = vs[t][g][i]
+    return cache
+
+
+def brute_attention_row(qrow, ks, vs, g, scale):
+    """softmax over keys of scale*q.k, then the weighted sum of V, with
+    Python floats and math.fsum (no numpy)."""
+    d = len(qrow)
+    scores = [scale * math.fsum(float(qrow[i]) * float(k[g][i]) for i in range(d)) for k in ks]
+    m = max(scores)
+    e = [math.exp(s - m) for s in scores]
+    z = math.fsum(e)
+    return [math.fsum(e[t] * float(vs[t][g][i]) for t in range(len(ks))) / z for i in range(d)]
+
+
+def _dense_stored(x_f32, dtype, O):
+    """Stored values as float64, derived with torch's own casts (not the
+    oracle's) for bf16/f16; int8 uses the quantizer under test."""
+    t = torch.from_numpy(np.ascontiguousarray(x_f32))
+    if dtype == "f32":
+        return t.double().numpy()
+    if dtype == "bf16":
+        return t.to(torch.bfloat16).double().numpy()
+    if dtype == "f16":
+        return t.to(torch.float16).double().numpy()
+    codes, sc = O.quantize_int8(x_f32)
+    return codes.astype(np.float64) * sc.astype(np.float64)[..., None]
+
+
+def _filled_cache(O, w, dtype=None):
+    c = O.PagedCache(w.num_pages, w.num_kv_heads, w.head_dim, dtype or w.kv_dtype)
+    O.ref_append(c, w.k, w.v, w.slot_mapping)
+    return c
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    """torch fp64 SDPA on the CPU; q [Hq, L, d], k/v [Hq, n, d]."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=None if mask is None else torch.from_numpy(mask)[None, None],
+        scale=scale)[0].numpy()
+
+
+# ------------------------------------------------------------------ attention pins
+def pin_bruteforce_decode(O):
+    w = custom_workload(context_lens=[1, 5, 37, 16], num_q_heads=4, num_kv_heads=2,
+                        head_dim=8, num_pages=12, seed=11)
+    ks = [_seq(w, w.k, b) for b in range(w.batch)]
+    vs = [_seq(w, w.v, b) for b in range(w.batch)]
+    cache = write_paged_f32(O, ks, vs, w.block_tables, w.num_pages, 2, 8)
+    out = O.ref_decode(w.q, cache, w.block_tables, w.context_lens, w.scale, 4)
+    for b in range(w.batch):
+        for h in range(4):
+            g = h * 2 // 4
+            ref = brute_attention_row(w.q[b, h], ks[b], vs[b], g, w.scale)
+            assert np.max(np.abs(out[b, h] - ref)) <= 1e-12, (b, h)
+
+
+def pin_bruteforce_prefill(O):
+    w = custom_workload(kind="prefill", context_lens=[9, 21, 18], q_lens=[9, 5, 1],
+                        num_q_heads=2, num_kv_heads=1, head_dim=4, num_pages=8, seed=12)
+    ks = [_seq(w, w.k, b) for b in range(w.batch)]
+    vs = [_seq(w, w.v, b) for b in range(w.batch)]
+    cache = write_paged_f32(O, ks, vs, w.block_tables, w.num_pages, 1, 4)
+    out = O.ref_prefill_chunk(w.q, cache, w.block_tables, w.context_lens, w.cu_q_lens, w.scale)
+    for b in range(w.batch):
+        n, C = int(w.context_lens[b]), int(w.q_lens[b])
+        P = n - C
+        for i in range(C):
+            row = int(w.cu_q_lens[b]) + i
+            for h in range(2):
+                ref = brute_attention_row(w.q[row, h], ks[b][:P + i + 1], vs[b][:P + i + 1], 0, w.scale)
+                assert np.max(np.abs(out[row, h] - ref)) <= 1e-12, (b, i, h)
+
+
+def pin_sdpa_decode_all_dtypes(O):
+    for dtype in ("f32", "bf16", "f16", "i8"):
+        w = custom_workload(context_lens=[16, 17, 33, 70], num_q_heads=6, num_kv_heads=2,
+                            head_dim=16, kv_dtype=dtype, num_pages=24, seed=13)
+        cache = _filled_cache(O, w)
+        out = O.ref_decode(w.q, cache, w.block_tables, w.context_lens, w.scale, 6)
+        for b in range(w.batch):
+            K = _dense_stored(_seq(w, w.k, b), dtype, O)
+            V = _dense_stored(_seq(w, w.v, b), dtype, O)
+            k = np.repeat(K.transpose(1, 0, 2), 3, axis=0)
+            v = np.repeat(V.transpose(1, 0, 2), 3, axis=0)
+            ref = _sdpa(w.q[b][:, None, :].astype(np.float64), k, v, w.scale)[:, 0, :]
+            assert np.max(np.abs(out[b] - ref)) <= 1e-12, (dtype, b)
+
+
+def pin_sdpa_prefill_bottom_right(O):
+    w = custom_workload(kind="prefill", context_lens=[20, 40, 35, 16], q_lens=[20, 17, 1, 16],
+                        num_q_heads=4, num_kv_heads=1, head_dim=8, num_pages=16, seed=14)
+    cache = _filled_cache(O, w)
+    out = O.ref_prefill_chunk(w.q, cache, w.block_tables, w.context_lens, w.cu_q_lens, w.scale)
+    for b in range(w.batch):
+        n, C = int(w.context_lens[b]), int(w.q_lens[b])
+        P = n - C
+        K = _seq(w, w.k, b).astype(np.float64)
+        V = _seq(w, w.v, b).astype(np.float64)
+        mask = np.array([[j <= P + i for j in range(n)] for i in range(C)])
+        r0 = int(w.cu_q_lens[b])
+        q = w.q[r0:r0 + C].transpose(1, 0, 2).astype(np.float64)
+        k = np.repeat(K.transpose(1, 0, 2), 4, axis=0)
+        v = np.repeat(V.transpose(1, 0, 2), 4, axis=0)
+        ref = _sdpa(q, k, v, w.scale, mask).transpose(1, 0, 2)
+        assert np.max(np.abs(out[r0:r0 + C] - ref)) <= 1e-12, b
+
+
+def pin_golden_closed_forms(O):
+    with open(os.path.join(GOLDEN, "attention_closed_forms.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        q = np.array(case["q"], dtype=np.float32)[None]          # [1, Hq, d]
+        k = np.array(case["k"], dtype=np.float32)                 # [n, Hkv, d]
+        v = np.array(case["v"], dtype=np.float32)
+        n, hkv, d = k.shape
+        bt = np.array([[3, 1]], dtype=np.int32)
+        cache = write_paged_f32(O, [k], [v], bt, 4, hkv, d)
+        out = O.ref_decode(q, cache, bt, np.array([n], np.int32), case["scale"], q.shape[1])
+        err = np.max(np.abs(out[0] - np.array(case["out"])))
+        assert err <= case["tol"], (case["name"], err)
+
+
+def pin_single_token_returns_v(O):
+    for dtype in ("f32", "bf16", "f16", "i8"):
+        w = custom_workload(context_lens=[1, 1, 1], num_q_heads=4, num_kv_heads=2,
+                            head_dim=16, kv_dtype=dtype, seed=15)
+        out = O.ref_decode(w.q, _filled_cache(O, w), w.block_tables, w.context_lens, w.scale, 4)
+        for b in range(3):
+            Vd = _dense_stored(_seq(w, w.v, b), dtype, O)[0]          # [Hkv, d]
+            assert np.array_equal(out[b], np.repeat(Vd, 2, axis=0)), (dtype, b)
+
+
+def pin_empty_context_is_zero(O):
+    w = custom_workload(context_lens=[0, 3, 0], num_q_heads=2, num_kv_heads=2, head_dim=8, seed=16)
+    out = O.ref_decode(w.q, _filled_cache(O, w), w.block_tables, w.context_lens, w.scale, 2)
+    assert np.all(out[0] == 0) and np.all(out[2] == 0) and np.any(out[1] != 0)
+
+
+def pin_scale_zero_is_mean(O):
+    w = custom_workload(context_lens=[7, 40], num_q_heads=3, num_kv_heads=1, head_dim=8,
+                        scale=0.0, seed=17)
+    out = O.ref_decode(w.q, _filled_cache(O, w), w.block_tables, w.context_lens, 0.0, 3)
+    for b in range(2):
+        mean = _seq(w, w.v, b).astype(np.float64).mean(axis=0)[0]
+        assert np.max(np.abs(out[b] - mean[None])) <= 1e-14
+
+
+def pin_shift_and_hull(O):
+    # V drawn on a coarse grid so that V + 1 is exact in fp32.
+    w = custom_workload(context_lens=[5, 33, 64], num_q_heads=2, num_kv_heads=1, head_dim=8, seed=18)
+    w.v[:] = np.round(w.v * 8) / 8
+    c0 = _filled_cache(O, w)
+    out0 = O.ref_decode(w.q, c0, w.block_tables, w.context_lens, w.scale, 2)
+    w.v[:] += 1.0
+    out1 = O.ref_decode(w.q, _filled_cache(O, w), w.block_tables, w.context_lens, w.scale, 2)
+    assert np.max(np.abs(out1 - (out0 + 1.0))) <= 1e-13
+    for b in range(w.batch):
+        V = _seq(w, w.v, b).astype(np.float64)[:, 0, :]
+        assert np.all(out1[b] >= V.min(axis=0) - 1e-13) and np.all(out1[b] <= V.max(axis=0) + 1e-13)
+
+
+def pin_page_permutation_invariance(O):
+    w = custom_workload(context_lens=[20, 50, 3], num_q_heads=4, num_kv_heads=2, head_dim=8,
+                        kv_dtype="bf16", num_pages=20, seed=19)
+    c = _filled_cache(O, w)
+    out = O.ref_decode(w.q, c, w.block_tables, w.context_lens, w.scale, 4)
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(w.num_pages)
+    inv = np.argsort(perm)               # new page p holds old page perm[p]
+    c2 = c.copy()
+    c2.k, c2.v = c.k[perm], c.v[perm]
+    bt2 = inv[w.block_tables].astype(np.int32)
+    out2 = O.ref_decode(w.q, c2, bt2, w.context_lens, w.scale, 4)
+    assert np.array_equal(out, out2)
+
+
+def pin_gqa_equals_repeated_mha(O):
+    w = custom_workload(context_lens=[9, 30], num_q_heads=6, num_kv_heads=2, head_dim=8, seed=20)
+    out = O.ref_decode(w.q, _filled_cache(O, w), w.block_tables, w.context_lens, w.scale, 6)
+    w.k = np.repeat(w.k, 3, axis=1)
+    w.v = np.repeat(w.v, 3, axis=1)
+    w.num_kv_heads = 6
+    out_mha = O.ref_decode(w.q, _filled_cache(O, w), w.block_tables, w.context_lens, w.scale, 6)
+    assert np.array_equal(out, out_mha)
+
+
+def pin_group_locality(O):
+    w = custom_workload(context_lens=[9, 30], num_q_heads=6, num_kv_heads=3, head_dim=8, seed=21)
+    out = O.ref_decode(w.q, _filled_cache(O, w), w.block_tables, w.context_lens, w.scale, 6)
+    w.v[:, 1, :] += 0.5
+    out2 = O.ref_decode(w.q, _filled_cache(O, w), w.block_tables, w.context_lens, w.scale, 6)
+    changed = np.any(out != out2, axis=(0, 2))
+    assert list(changed) == [False, False, True, True, False, False], changed
+
+
+def pin_causal_structure(O):
+    w = custom_workload(kind="prefill", context_lens=[45], q_lens=[20], num_q_heads=2,
+                        num_kv_heads=1, head_dim=8, seed=22)
+    P = 25
+    out = O.ref_prefill_chunk(w.q, _filled_cache(O, w), w.block_tables, w.context_lens,
+                              w.cu_q_lens, w.scale)
+    for p in (P + 3, P + 11, 44):
+        w2 = custom_workload(kind="prefill", context_lens=[45], q_lens=[20], num_q_heads=2,
+                             num_kv_heads=1, head_dim=8, seed=22)
+        w2.k[p] += 2.0
+        w2.v[p] -= 3.0
+        out2 = O.ref_prefill_chunk(w2.q, _filled_cache(O, w2), w2.block_tables,
+                                   w2.context_lens, w2.cu_q_lens, w2.scale)
+        for i in range(20):
+            same = np.array_equal(out[i], out2[i])
+            assert same == (P + i < p), (p, i)
+
+
+def pin_prefill_row_equals_decode(O):
+    w = custom_workload(kind="prefill", context_lens=[37, 16], q_lens=[12, 16], num_q_heads=4,
+                        num_kv_heads=2, head_dim=8, seed=23)
+    c = _filled_cache(O, w)
+    out = O.ref_prefill_chunk(w.q, c, w.block_tables, w.context_lens, w.cu_q_lens, w.scale)
+    for b in range(2):
+        n, C = int(w.context_lens[b]), int(w.q_lens[b])
+        for i in range(C):
+            row = int(w.cu_q_lens[b]) + i
+            dec = O.ref_decode(w.q[row][None], c, w.block_tables[b:b + 1],
+                               np.array([n - C + i + 1], np.int32), w.scale, 4)
+            assert np.max(np.abs(out[row] - dec[0])) <= 1e-13, (b, i)
+    # P = 0, i = 0 attends to the first token only
+    b1 = int(w.cu_q_lens[1])
+    v0 = _seq(w, w.v, 1)[0].astype(np.float64)
+    assert np.array_equal(out[b1], np.repeat(v0, 2, axis=0))
+
+
+def pin_chunk_split(O):
+    w = custom_workload(kind="prefill", context_lens=[50], q_lens=[30], num_q_heads=2,
+                        num_kv_heads=1, head_dim=8, seed=24)
+    c = _filled_cache(O, w)
+    full = O.ref_prefill_chunk(w.q, c, w.block_tables, w.context_lens, w.cu_q_lens, w.scale)
+    a = O.ref_prefill_chunk(w.q[:11], c, w.block_tables, np.array([31], np.int32),
+                            np.array([0, 11], np.int32), w.scale)
+    b = O.ref_prefill_chunk(w.q[11:], c, w.block_tables, np.array([50], np.int32),
+                            np.array([0, 19], np.int32), w.scale)
+    assert np.max(np.abs(np.concatenate([a, b]) - full)) <= 1e-13
+
+
+# ------------------------------------------------------------------ conversion pins
+def _golden_conv():
+    with open(os.path.join(GOLDEN, "conversions.json")) as f:
+        return json.load(f)
+
+
+def pin_bf16_golden_and_torch(O):
+    for case in _golden_conv()["bf16"]:
+        x = np.array([int(case["f32_bits"], 16)], dtype=np.uint32).view(np.float32)
+        got = int(O.f32_to_bf16_bits(x)[0])
+        assert got == int(case["bf16_bits"], 16), case
+    rng = np.random.Generator(np.random.PCG64(30))
+    x = np.concatenate([rng.standard_normal(20000, dtype=np.float32),
+                        rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32).view(np.float32)])
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f32_to_bf16_bits(x), ref)
+    assert np.array_equal(O.bf16_bits_to_f64(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+def pin_f16_golden_and_torch(O):
+    for case in _golden_conv()["f16"]:
+        got = int(O.f32_to_f16(np.array([case["value"]], np.float32)).view(np.uint16)[0])
+        assert got == int(case["f16_bits"], 16), case
+    rng = np.random.Generator(np.random.PCG64(31))
+    x = np.concatenate([rng.standard_normal(20000, dtype=np.float32),
+                        (rng.standard_normal(20000) * 1e-5).astype(np.float32),
+                        (rng.standard_normal(2000) * 7e4).astype(np.float32)])
+    ref = torch.from_numpy(x).to(torch.float16).numpy()
+    assert np.array_equal(O.f32_to_f16(x).view(np.uint16), ref.view(np.uint16))
+
+
+def pin_int8_golden(O):
+    for case in _golden_conv()["int8"]:
+        codes, sc = O.quantize_int8(np.array([case["x"]], np.float32))
+        assert float(sc[0]) == case["scale"], case
+        assert codes[0].tolist() == case["codes"], case
+
+
+def pin_int8_bounds(O):
+    rng = np.random.Generator(np.random.PCG64(32))
+    x = rng.standard_normal((3000, 64), dtype=np.float32)
+    codes, sc = O.quantize_int8(x)
+    s = sc.astype(np.float64)[:, None]
+    assert np.all(np.abs(x - codes * s) <= s * (0.5 + 1e-5))
+    assert np.all(np.abs(codes[np.arange(3000), np.argmax(np.abs(x), axis=1)]) == 127)
+    assert np.all(np.abs(codes) <= 127)
+    c2, s2 = O.quantize_int8(-x)
+    assert np.array_equal(c2, -codes) and np.array_equal(s2, sc)
+
+
+def pin_append_layout(O):
+    w = custom_workload(context_lens=[19, 33], num_q_heads=2, num_kv_heads=2, head_dim=8,
+                        num_pages=8, seed=33)
+    slots = w.slot_mapping.copy()
+    slots[[3, 20]] = -1                  # padding tokens are skipped
+    c = O.PagedCache(w.num_pages, 2, 8, "f32")
+    O.ref_append(c, w.k, w.v, slots)
+    e = O.PagedCache(w.num_pages, 2, 8, "f32")
+    for j, s in enumerate(slots):
+        if s < 0:
+            continue
+        for g in range(2):
+            for i in range(8):
+                e.k[s // PS, g, s % PS, i] = w.k[j, g, i]
+                e.v[s // PS, g, i, s % PS] = w.v[j, g, i]
+    assert np.array_equal(c.k, e.k) and np.array_equal(c.v, e.v)
+    ci = O.PagedCache(w.num_pages, 2, 8, "i8")
+    O.ref_append(ci, w.k, w.v, slots)
+    for j, s in enumerate(slots):
+        if s < 0:
+            continue
+        kq, ks = O.quantize_int8(w.k[j])
+        vq, vs = O.quantize_int8(w.v[j])
+        assert np.array_equal(ci.k[s // PS, :, s % PS, :], kq)
+        assert np.array_equal(ci.v[s // PS, :, :, s % PS], vq)
+        assert np.array_equal(ci.k_scales[s // PS, :, s % PS], ks)
+        assert np.array_equal(ci.v_scales[s // PS, :, s % PS], vs)
+    for s in w.slot_mapping[[3, 20]]:
+        assert np.all(ci.k[s // PS, :, s % PS, :] == 0) and np.all(ci.v_scales[s // PS, :, s % PS] == 0)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

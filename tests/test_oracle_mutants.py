@@ -1,0 +1,59 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is the oracle's source with one plausible slip (a wrong index,
+a dropped term, a wrong rounding), executed into a fresh module on the CPU.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle.paged_attention as O
+from oracle_pins import ALL_PINS
+
+SRC = inspect.getsource(O)
+
+MUTANTS = [
+    ("gqa_map_modulo_decode", "            g = h // G\n            s = sc * (K[:, g, :] @ q[b, h])",
+     "            g = h % cache.num_kv_heads\n            s = sc * (K[:, g, :] @ q[b, h])"),
+    ("gqa_map_modulo_prefill", "            g = h // G\n            s = sc * (q[r0:r1",
+     "            g = h % cache.num_kv_heads\n            s = sc * (q[r0:r1"),
+    ("dropped_scale", "s = sc * (K[:, g, :] @ q[b, h])", "s = (K[:, g, :] @ q[b, h])"),
+    ("causal_strict", "keypos <= rowpos", "keypos < rowpos"),
+    ("causal_top_left", "rowpos = P + np.arange(C)[:, None]", "rowpos = np.arange(C)[:, None]"),
+    ("excludes_current_token", "n = int(context_lens[b])\n        if n == 0:",
+     "n = int(context_lens[b]) - 1\n        if n <= 0:"),
+    ("wrong_normalisation", "return e / np.sum(e, axis=-1, keepdims=True)",
+     "return e / np.max(e, axis=-1, keepdims=True)"),
+    ("page_index_off", "page = np.asarray(block_row, dtype=np.int64)[t // PAGE_SIZE]",
+     "page = np.asarray(block_row, dtype=np.int64)[(t + 1) // PAGE_SIZE]"),
+    ("v_layout_not_transposed", "V = upcast(cache.v[page, :, :, off], cache.dtype, vs)",
+     "V = upcast(cache.v.reshape(cache.v.shape[0], cache.v.shape[1], PAGE_SIZE, -1)[page, :, off, :], cache.dtype, vs)"),
+    ("swapped_int8_scales", "cache.k_scales[page, :, off] = ks", "cache.k_scales[page, :, off] = vs"),
+    ("int8_scale_128", "(absmax / np.float32(127.0))", "(absmax / np.float32(128.0))"),
+    ("int8_truncates", "np.clip(np.rint(ratio), -127, 127)", "np.clip(np.trunc(ratio), -127, 127)"),
+    ("int8_dequant_divides", "np.asarray(stored, dtype=np.int8).astype(np.float64) * \\",
+     "np.asarray(stored, dtype=np.int8).astype(np.float64) / \\"),
+    ("bf16_round_half_up", "(u + 0x7FFF + ((u >> 16) & 1)) >> 16", "(u + 0x8000) >> 16"),
+    ("bf16_truncates", "(u + 0x7FFF + ((u >> 16) & 1)) >> 16", "u >> 16"),
+    ("append_ignores_padding", "keep = slots >= 0", "keep = slots >= -1"),
+]
+
+
+def _mutant_module(old, new):
+    assert SRC.count(old) == 1, f"mutation target must occur once: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    mod = _mutant_module(old, new)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception:        # an assertion or a crash both count as caught
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
