@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+Headline workload: paged decode with a bf16 KV cache at the Qwen2.5-1.5B
+attention shape (batch 64, 12 query / 2 KV heads, head_dim 128, 16-token
+pages, context lengths uniform in [512, 4096], pages scattered over a
+20k-page pool).  One step = append of the step's 64 new tokens + the decode
+call (partition kernel + log-sum-exp reduce).  Before every timed step a
+1 GiB read-modify-write evicts L2 and the 256 MB MALL, so every step reads
+its KV from HBM; each step is timed with HIP events on the stream the
+library launches on (the flush is outside the events).
+
+value = effective KV bytes (sum of context tokens x KV heads x head_dim x
+2 (K and V) x bytes per element) / mean step time, in GB/s.
+
+Also reported in the same line: the chunked-prefill workload (8 x 512-token
+bf16 chunks over prefixes uniform in [0, 3584], Qwen2.5-1.5B heads) in
+algorithmic TFLOP/s, the other decode shapes (fp16-KV Stories110M shape,
+int8-KV TinyLlama shape, small fp32 case), the roofline of each dominant
+kernel, and the CPU oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ELEM = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1}
+DESC = {
+    "C1": "paged decode, fp32 q/KV/out, batch 4, 9 q / 3 KV heads, head_dim 64, ctx {17,64,133,200}",
+    "C2": "paged decode, bf16 KV + fp32 accumulation, Qwen2.5-1.5B shape: batch 64, 12 q / 2 KV heads, head_dim 128, ctx U[512,4096], 20k-page pool",
+    "C3": "paged decode, fp16 KV, Stories110M shape: batch 384, 12 q / 12 KV heads, head_dim 64, ctx U[64,1024]",
+    "C4": "chunked causal prefill, bf16 q/KV, Qwen2.5-1.5B shape: 8 x 512-token chunks over prefixes U[0,3584], 12 q / 2 KV heads, head_dim 128",
+    "C5": "paged decode, int8 KV + per-token-head fp32 scales, TinyLlama-1.1B shape: batch 128, 32 q / 4 KV heads, head_dim 64, ctx 2048",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def effective_kv_bytes(w) -> int:
+    tok = int(w.context_lens.astype(int).sum())
+    b = tok * w.num_kv_heads * w.head_dim * 2 * ELEM[w.kv_dtype]
+    if w.kv_dtype == "i8":
+        b += tok * w.num_kv_heads * 2 * 4
+    return b
+
+
+def prefill_flops(w) -> int:
+    total = 0
+    for b in range(w.batch):
+        C = int(w.q_lens[b])
+        P = int(w.context_lens[b]) - C
+        total += C * P + C * (C + 1) // 2          # sum_i (P + i + 1)
+    return 4 * w.head_dim * w.num_q_heads * total
+
+
+def source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_attention_10_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(profile_name: str, sha: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"^source_sha256:\s*(\S+)", text, re.M)
+    m_tr = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_sha or not m_tr or m_sha.group(1) != sha:
+        return None
+    return float(m_tr.group(1))
+
+
+class Gpu:
+    def __init__(self):
+        import torch
+        import paged_kv_attention_10_amd as pkv
+        self.torch, self.pkv = torch, pkv
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        self.flush_buf = torch.zeros(256 * 1024 * 1024, dtype=torch.float32, device=self.dev)
+
+    def flush(self):
+        self.flush_buf.add_(1.0)        # 1 GiB read + write: evicts L2 and MALL
+
+    def t(self, a):
+        return self.torch.from_numpy(a).to(self.dev)
+
+    def pool(self, w):
+        torch = self.torch
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i8": torch.int8}[w.kv_dtype]
+        k = torch.zeros((w.num_pages, w.num_kv_heads, 16, w.head_dim), dtype=dt, device=self.dev)
+        v = torch.zeros((w.num_pages, w.num_kv_heads, w.head_dim, 16), dtype=dt, device=self.dev)
+        ks = vs = None
+        if w.kv_dtype == "i8":
+            ks = torch.zeros((w.num_pages, w.num_kv_heads, 16), dtype=torch.float32, device=self.dev)
+            vs = torch.zeros_like(ks)
+        return k, v, ks, vs
+
+    def fill_pool(self, w, pool, rows):
+        """Append the tokens at `rows` (fp32 K/V) into the pool on the GPU."""
+        k, v, ks, vs = pool
+        step = 1 << 17
+        for i in range(0, len(rows), step):
+            r = rows[i:i + step]
+            self.pkv.paged_kv_append(self.t(w.k[r]), self.t(w.v[r]), self.t(w.slot_mapping[r]),
+                                     k, v, ks, vs)
+        self.torch.cuda.synchronize()
+
+    def timed_steps(self, step_fn, inner_fn, steps, warmup, flush=True):
+        """Run warmup + steps; each step is flushed (outside the events) and
+        bracketed by events; `inner_fn` is the dominant call, bracketed by its
+        own pair of events inside the step."""
+        torch = self.torch
+        for _ in range(warmup):
+            if flush:
+                self.flush()
+            step_fn(inner_fn)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush:
+                self.flush()
+            e0, e1, e2, e3 = ev[i]
+            e0.record()
+            step_fn(inner_fn, e1, e2)
+            e3.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = [e[0].elapsed_time(e[3]) for e in ev]
+        inner_ms = [e[1].elapsed_time(e[2]) for e in ev]
+        return step_ms, inner_ms, wall
+
+
+def stats(xs):
+    s = sorted(xs)
+    n = len(s)
+    return {"mean": sum(s) / n, "median": s[n // 2], "p10": s[int(0.1 * (n - 1))],
+            "p90": s[int(0.9 * (n - 1))]}
+
+
+def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
+    from workloads import make_workload
+    w = make_workload(name)
+    log(f"[bench] {name}: building the pool on the GPU")
+    pool = g.pool(w)
+    new_rows = w.new_token_rows()
+    old_mask = g.torch.ones(len(w.slot_mapping), dtype=g.torch.bool).numpy()
+    old_mask[new_rows] = False
+    g.fill_pool(w, pool, old_mask.nonzero()[0])
+    k, v, ks, vs = pool
+    k_new, v_new = g.t(w.k[new_rows]), g.t(w.v[new_rows])
+    slots_new = g.t(w.slot_mapping[new_rows])
+    q = g.t(w.q)
+    bt, cl = g.t(w.block_tables), g.t(w.context_lens)
+    out = g.torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=g.torch.float32, device=g.dev)
+    nws = g.pkv.paged_attn_decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads,
+                                                  w.head_dim, w.max_context_len)
+    ws = g.torch.empty(max(nws, 16), dtype=g.torch.uint8, device=g.dev)
+
+    def decode():
+        g.pkv.paged_attn_decode(q, k, v, bt, cl, w.max_context_len, w.scale, out=out,
+                                k_scales=ks, v_scales=vs, workspace=ws)
+
+    def step(inner, e1=None, e2=None):
+        g.pkv.paged_kv_append(k_new, v_new, slots_new, k, v, ks, vs)
+        if e1 is not None:
+            e1.record()
+        inner()
+        if e2 is not None:
+            e2.record()
+
+    log(f"[bench] {name}: {warmup} warmup + {steps} timed steps")
+    step_ms, inner_ms, wall = g.timed_steps(step, decode, steps, warmup)
+    nbytes = effective_kv_bytes(w)
+    st, si = stats(step_ms), stats(inner_ms)
+    res = {
+        "workload": name, "desc": DESC[name], "effective_kv_bytes": nbytes,
+        "ms_per_step": st["mean"], "step_ms": st, "decode_call_ms": si,
+        "kv_gbs": nbytes / (st["mean"] * 1e-3) / 1e9,
+        "seq_tokens_per_s": w.batch / (st["mean"] * 1e-3),
+        "context_tokens_per_s": float(w.context_lens.sum()) / (st["mean"] * 1e-3),
+        "decode_call_gbs": nbytes / (si["mean"] * 1e-3) / 1e9,
+        "wall_s_timed_region": wall,
+        "plan_workspace_bytes": int(nws),
+    }
+    res["hbm_frac_step"] = res["kv_gbs"] / HBM_PEAK_GBS
+    return w, res, out
+
+
+def bench_prefill(g: Gpu, steps: int, warmup: int):
+    from workloads import make_workload
+    w = make_workload("C4")
+    log("[bench] C4: building the prefix pool on the GPU")
+    pool = g.pool(w)
+    new_rows = w.new_token_rows()
+    old_mask = g.torch.ones(len(w.slot_mapping), dtype=g.torch.bool).numpy()
+    old_mask[new_rows] = False
+    g.fill_pool(w, pool, old_mask.nonzero()[0])
+    k, v, _, _ = pool
+    k_new, v_new = g.t(w.k[new_rows]), g.t(w.v[new_rows])
+    slots_new = g.t(w.slot_mapping[new_rows])
+    q = g.t(w.q).to(g.torch.bfloat16)
+    bt, cl, cu = g.t(w.block_tables), g.t(w.context_lens), g.t(w.cu_q_lens)
+    out = g.torch.empty((w.num_query_tokens, w.num_q_heads, w.head_dim), dtype=g.torch.float32,
+                        device=g.dev)
+
+    def prefill():
+        g.pkv.paged_attn_prefill_chunk(q, k, v, bt, cl, cu, w.max_q_len, w.max_context_len,
+                                       w.scale, out=out)
+
+    def step(inner, e1=None, e2=None):
+        g.pkv.paged_kv_append(k_new, v_new, slots_new, k, v)
+        if e1 is not None:
+            e1.record()
+        inner()
+        if e2 is not None:
+            e2.record()
+
+    log(f"[bench] C4: {warmup} warmup + {steps} timed steps")
+    step_ms, inner_ms, wall = g.timed_steps(step, prefill, steps, warmup)
+    flops = prefill_flops(w)
+    st, si = stats(step_ms), stats(inner_ms)
+    res = {
+        "workload": "C4", "desc": DESC["C4"], "algorithmic_flops": flops,
+        "prefix_lens": w.meta["prefix_lens"].tolist(),
+        "ms_per_step": st["mean"], "step_ms": st, "prefill_call_ms": si,
+        "tflops_step": flops / (st["mean"] * 1e-3) / 1e12,
+        "tflops_prefill_call": flops / (si["mean"] * 1e-3) / 1e12,
+        "prefill_tokens_per_s": w.num_query_tokens / (st["mean"] * 1e-3),
+        "wall_s_timed_region": wall,
+    }
+    res["roofline"] = {"bound": "mfma", "achieved": res["tflops_prefill_call"],
+                       "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": res["tflops_prefill_call"] / BF16_PEAK_TFLOPS,
+                       "traffic": profiled_traffic("prefill_C4_counters.txt",
+                                                   source_sha("prefill.hip"))}
+    return w, res, out
+
+
+def cpu_baseline(w, gpu_out, budget_s: float):
+    """The oracle as it stands, timed on the host: one step = oracle append
+    of the step's new tokens + oracle decode of the whole batch, repeated
+    until `budget_s` of CPU work; also the parity of the GPU output."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle
+    log("[bench] cpu baseline: oracle cache build (untimed)")
+    cache = oracle.PagedCache(w.num_pages, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    new_rows = w.new_token_rows()
+    old = np.ones(len(w.slot_mapping), dtype=bool)
+    old[new_rows] = False
+    oracle.ref_append(cache, w.k[old], w.v[old], w.slot_mapping[old])
+    times = []
+    ref = None
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        oracle.ref_append(cache, w.k[new_rows], w.v[new_rows], w.slot_mapping[new_rows])
+        ref = oracle.ref_decode(w.q, cache, w.block_tables, w.context_lens, w.scale,
+                                w.num_q_heads)
+        times.append(time.perf_counter() - t0)
+        log(f"[bench] cpu baseline step {len(times)}: {times[-1]:.2f} s")
+        if time.perf_counter() >= t_end:
+            break
+    mean = sum(times) / len(times)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    err = oracle.max_abs_err(gpu_out.double().cpu().numpy(), ref)
+    return {
+        "value": effective_kv_bytes(w) / mean / 1e9, "unit": "GB/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"the whole {w.name} batch ({w.batch} sequences), oracle append of the "
+                  f"step's {len(new_rows)} new tokens + fp64 numpy decode, {len(times)} steps "
+                  f"in {sum(times):.1f} s; affinity {len(os.sched_getaffinity(0))} cores",
+        "seconds_per_step": mean,
+        "gpu_vs_oracle_max_abs_err": err,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle CPU work for the baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="comma list of workloads to run (C1..C5); default all")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5"}
+
+    g = Gpu()
+    extras = {}
+    head = None
+    if "C2" in only:
+        w2, head, out2 = bench_decode(g, "C2", args.steps, args.warmup)
+    for name in ("C3", "C5", "C1"):
+        if name in only:
+            _, r, _ = bench_decode(g, name, args.steps, args.warmup)
+            r["roofline"] = {"bound": "hbm", "achieved": r["decode_call_gbs"], "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": r["decode_call_gbs"] / HBM_PEAK_GBS,
+                             "traffic": profiled_traffic(f"decode_{name}_counters.txt",
+                                                         source_sha("decode.hip"))}
+            extras[f"decode_{name}"] = r
+    if "C4" in only:
+        _, rp, _ = bench_prefill(g, args.steps, args.warmup)
+        extras["prefill_C4"] = rp
+
+    line = {
+        "metric": "decode KV GB/s (% HBM peak) + seq-tokens/s; prefill TFLOP/s (% MFMA)",
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) q/K/V, scattered page tables)",
+    }
+    if head is not None:
+        line.update({
+            "value": round(head["kv_gbs"], 2),
+            "ms_per_step": round(head["ms_per_step"], 5),
+            "config": {"workload": DESC["C2"], "batch": 64, "num_q_heads": 12, "num_kv_heads": 2,
+                       "head_dim": 128, "page_size": 16, "kv_dtype": "bf16",
+                       "context_tokens": int(w2.context_lens.sum()),
+                       "step": "append of 64 new tokens + decode (partition + LSE reduce)",
+                       "timing": "HIP events per step on the library's stream; 1 GiB flush before each step, outside the events"},
+            "hbm_frac": round(head["hbm_frac_step"], 4),
+            "seq_tokens_per_s": round(head["seq_tokens_per_s"], 1),
+            "roofline": {"bound": "hbm", "achieved": round(head["decode_call_gbs"], 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(head["decode_call_gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("decode_C2_counters.txt",
+                                                     source_sha("decode.hip")),
+                         "kernel": "paged_attn_decode call (decode_partition_kernel<128,bf16> + decode_reduce_kernel<128>)",
+                         "algorithmic_bytes_per_launch": head["effective_kv_bytes"]},
+            "detail_C2": head,
+        })
+    line["extra"] = extras
+    if head is not None and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w2, out2, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

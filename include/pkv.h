@@ -1,0 +1,198 @@
+/*
+ * pkv.h - attention over a paged KV cache on MI355X (gfx950), C ABI.
+ *
+ * The operation: softmax(q K^T * scale) V over a KV cache held in fixed
+ * 16-token pages that each sequence indexes through its row of a block table
+ * (TinyLoop "Current Status", table "KV cache modes", row "Paged attention":
+ * 16-token pages).  Two query shapes are served: batched decode, one query
+ * token per sequence (same page, table "Core inference", row "Generation";
+ * mini-llm README, architecture overview: true batched decode), and chunked
+ * causal prefill, a block of query tokens over its paged prefix (TinyLoop
+ * "Current Status", table "Model architecture support", row "Chunked
+ * prefill"; Tiny-LLM "Project Status", supported-features list).  Query heads
+ * share KV heads in groups (GQA/MQA; TinyLoop table "Model architecture
+ * support", row "GQA").  KV storage is fp32, bf16, fp16 or int8 with
+ * per-token-per-head fp32 scales (Tiny-LLM "Project Status", dtype-contract
+ * paragraph; mini-llm README hardware table, FP16 KV cache; TinyLoop table
+ * "KV cache modes", row "INT8 KV cache").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor pointer is a device pointer (HBM) allocated by the
+ * caller, dense and row-major in the layout stated, aligned to 16 bytes.
+ * The library never allocates, frees or synchronises, and keeps no pointer
+ * after it returns.  All work is enqueued, in order, on `stream` (a
+ * hipStream_t; NULL is the null stream) and the call returns without
+ * waiting.  Calls on one stream are ordered; calls on different streams that
+ * write the same buffers race.
+ *
+ * Cache layout (page size 16, the only size built):
+ *   k_cache   [num_pages][num_kv_heads][16][head_dim]   token-major page
+ *   v_cache   [num_pages][num_kv_heads][head_dim][16]   token index innermost
+ *   k_scales, v_scales [num_pages][num_kv_heads][16] float32 (int8 only)
+ * Token t of sequence b lives in page block_tables[b][t / 16] at offset
+ * t % 16.  The V page is stored with tokens innermost so that the PV
+ * contraction (over tokens) reads contiguous runs.
+ *
+ * GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued;
+ * a non-zero status means nothing was launched.  Device-resident data
+ * (context lengths, block-table entries, slots) is not read by the host.  A
+ * kernel that meets an out-of-range page id or a context length beyond the
+ * block-table row or beyond max_context_len writes NaN for the affected
+ * outputs instead of reading out of bounds; an append slot outside the pool
+ * is skipped.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+#define PKV_PAGE_SIZE 16
+
+/* Element types.  PKV_BF16 is bfloat16 bits, PKV_I8 is int8 codes (KV only). */
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_F16 = 2, PKV_I8 = 3 };
+
+/* Status codes. */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,          /* null pointer, non-positive size, Hq % Hkv != 0, ... */
+  PKV_ERR_UNSUPPORTED = 2,          /* page size, head_dim or dtype combination not built */
+  PKV_ERR_MISALIGNED = 3,           /* a tensor pointer is not 16-byte aligned */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace_bytes below the size the query returns */
+  PKV_ERR_HIP = 5                   /* a kernel launch failed */
+};
+
+typedef struct ihipStream_t* pkv_stream_t; /* the same type as hipStream_t */
+
+/* ABI version of the loaded library (PKV_ABI_VERSION at build time). */
+int pkv_abi_version(void);
+
+/* Static, human-readable name of a status code; never NULL. */
+const char* pkv_status_string(int status);
+
+/*
+ * paged_kv_append - write new K/V tokens into the pool through a slot map.
+ *
+ * Defines the write side of the paged cache: each new token of a sequence
+ * is stored in a page slot of the pool (TinyLoop "Current Status", table "KV
+ * cache modes", rows "Paged attention" and "INT8 KV cache"), converted to
+ * the cache's dtype (Tiny-LLM "Project Status", dtype-contract paragraph).
+ *
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim], dtype new_dtype
+ *                  (PKV_F32, PKV_BF16 or PKV_F16); read only.
+ *   slot_mapping   [num_tokens] int64; token j goes to page slot/16, offset
+ *                  slot%16.  A negative slot skips the token (padding); a
+ *                  slot >= num_pages*16 is skipped too.  Two tokens with the
+ *                  same slot in one call leave either one (undefined which).
+ *   k_cache, v_cache  the pool (layout above), dtype cache_dtype; written.
+ *   k_scales, v_scales  required (non-NULL) iff cache_dtype == PKV_I8, and
+ *                  must be NULL otherwise; written.
+ *
+ * Conversions: fp32 is copied bit for bit; fp16 and bf16 round to nearest
+ * even (fp16 keeps subnormals; a bf16 NaN stays NaN); int8 is symmetric
+ * absmax per (token, KV head): scale = absmax/127 in IEEE fp32, code =
+ * clamp(rint(x/scale), -127, 127) with ties to even, scale 0 and codes 0 for
+ * an all-zero vector; the int8 result for a vector holding inf or NaN is
+ * unspecified.  num_tokens == 0 is a no-op returning PKV_OK.
+ */
+int paged_kv_append(const void* k_new, const void* v_new, int new_dtype,
+                    const int64_t* slot_mapping, int num_tokens,
+                    void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                    int cache_dtype, int num_pages, int num_kv_heads, int head_dim,
+                    int page_size, pkv_stream_t stream);
+
+/*
+ * paged_attn_decode - one query token per sequence over its paged context.
+ *
+ * Batched cached decode (TinyLoop "Current Status", table "Core inference",
+ * row "Generation"; mini-llm README, true batched decode) over 16-token pages
+ * with GQA.  context_lens[b] counts the query token itself, whose K/V must
+ * already be appended; the query attends to positions [0, context_lens[b]).
+ * A sequence with context_lens[b] == 0 gets zeros.
+ *
+ *   q              [batch][num_q_heads][head_dim], dtype q_dtype (F32/BF16/F16).
+ *   k_cache, v_cache, k_scales, v_scales, kv_dtype   the pool (layout above);
+ *                  scales non-NULL iff kv_dtype == PKV_I8.
+ *   block_tables   [batch][max_blocks_per_seq] int32 page ids; entries past a
+ *                  sequence's last page are never read.
+ *   context_lens   [batch] int32, each in [0, max_context_len].
+ *   max_context_len  host-side upper bound of context_lens, at most
+ *                  max_blocks_per_seq*16; sizes the split of long contexts.
+ *   num_pages      pool size in pages (page ids must be below it).
+ *   scale          multiplies q.k before the softmax.
+ *   out            [batch][num_q_heads][head_dim], dtype out_dtype (F32/BF16/F16).
+ *   workspace      device scratch of at least
+ *                  paged_attn_decode_workspace_bytes(...) bytes (may be NULL
+ *                  when that is 0); its contents on entry do not matter.
+ *
+ * Built for head_dim 64 and 128, page_size 16, any num_q_heads/num_kv_heads
+ * ratio.  Long contexts are split into partitions whose softmax partials
+ * are merged by a log-sum-exp reduction on the same stream.
+ */
+int paged_attn_decode(const void* q, int q_dtype,
+                      const void* k_cache, const void* v_cache,
+                      const float* k_scales, const float* v_scales, int kv_dtype,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int max_context_len,
+                      int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                      int page_size, int num_pages, float scale,
+                      void* out, int out_dtype,
+                      void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
+/* Workspace bytes paged_attn_decode needs for these shapes (0 when the
+ * contexts fit one partition).  Pure host arithmetic; touches no device. */
+size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int max_context_len);
+
+/*
+ * paged_attn_prefill_chunk - a causal chunk of query tokens over its paged
+ * prefix.
+ *
+ * Chunked prefill (TinyLoop "Current Status", table "Model architecture
+ * support", row "Chunked prefill"; Tiny-LLM "Project Status", supported
+ * features: chunked prefill/decode scheduling with a paged KV cache).  The
+ * chunk's own K/V must already be appended.  Sequence b's queries are rows
+ * cu_q_lens[b] .. cu_q_lens[b+1]-1 of q; with C_b = cu_q_lens[b+1]-cu_q_lens[b]
+ * and P_b = context_lens[b] - C_b (required >= 0), chunk row i sits at
+ * absolute position P_b + i and attends to positions [0, P_b + i].
+ *
+ *   q              [num_tokens][num_q_heads][head_dim], dtype q_dtype.
+ *   cu_q_lens      [batch+1] int32, cu_q_lens[0] == 0, non-decreasing,
+ *                  cu_q_lens[batch] == num_tokens, each C_b <= max_q_len.
+ *   context_lens   [batch] int32 = P_b + C_b, each <= max_context_len.
+ *   out            [num_tokens][num_q_heads][head_dim], dtype out_dtype.
+ *   workspace      at least paged_attn_prefill_workspace_bytes(...) bytes.
+ *   other arguments as for paged_attn_decode.
+ *
+ * Built for head_dim 64 and 128, page_size 16, kv_dtype PKV_BF16 or PKV_F16
+ * (QK^T and PV on MFMA with fp32 accumulation); other KV dtypes return
+ * PKV_ERR_UNSUPPORTED.
+ */
+int paged_attn_prefill_chunk(const void* q, int q_dtype,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scales, const float* v_scales, int kv_dtype,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* cu_q_lens,
+                             int num_tokens, int max_q_len, int max_context_len,
+                             int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                             int page_size, int num_pages, float scale,
+                             void* out, int out_dtype,
+                             void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
+/* Workspace bytes paged_attn_prefill_chunk needs (pure host arithmetic). */
+size_t paged_attn_prefill_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
+                                          int head_dim, int max_q_len, int max_context_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

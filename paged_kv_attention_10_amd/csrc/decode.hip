@@ -1,0 +1,504 @@
+// Batched paged decode: one query token per sequence attends over its
+// 16-token pages with GQA (TinyLoop "Current Status", tables "Core
+// inference" row "Generation", "KV cache modes" row "Paged attention",
+// "Model architecture support" row "GQA").
+//
+// Work split.  A workgroup of 4 waves owns one (sequence b, KV head g, tile
+// of up to 16 query heads, context split).  The context is walked in tiles
+// of 32 tokens (two pages); wave w takes tiles w, w+4, ... of its split and
+// keeps its own running max / sum / accumulator.  The four waves merge in
+// LDS; a sequence whose context needs several splits writes normalised
+// partials plus a log2-sum-exp per split, merged by decode_reduce_kernel.
+//
+// MFMA mapping (16x16 tiles, wave64).  Scores are computed transposed,
+// S^T = K * Q^T: A = K (row = token), B = Q^T (column = query head of the
+// group, padded to 16).  The output layout puts, in lane (c + 16*j), the
+// scores of head c for the 8 consecutive tile tokens 8j..8j+7 - exactly the
+// B-operand layout PV needs, so O^T = V^T * P^T runs with no data movement:
+// A = V^T (row = d), B = P^T.  The V page is stored token-innermost, so every
+// A-operand load of V^T is a contiguous 8-token run.  The A-operand row of
+// K for tile token tau is chosen so that this holds: MFMA u (0/1), row r
+// loads token 8*(r/4) + 4*u + r%4.
+//
+// Precision.  bf16/fp16 KV use the 16x16x32 MFMA; the fp32 query and the
+// fp32 probabilities are each split into a 16-bit head plus remainder and
+// multiplied twice, so products carry ~16 significant bits.  int8 codes are
+// converted exactly to fp16; the per-token K scale multiplies the score and
+// the per-token V scale folds into the probability.  fp32 KV uses the fp32
+// 16x16x4 MFMA.  exp is exp2 of a log2e-prescaled score.
+#include <math.h>
+
+#include <type_traits>
+
+#include "pkv_device.h"
+#include "pkv_host.h"
+
+namespace pkv {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scales;
+  const float* v_scales;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* part_o;
+  float* part_lse;
+  int q_dtype, out_dtype;
+  int max_blocks, max_context_len;
+  int batch, hq, hkv, group, head_tiles, num_pages;
+  int tiles_per_split, nsplits;
+  float scale_log2;
+};
+
+// Context length as the kernels use it; flags lengths the block table
+// cannot hold.
+__device__ __forceinline__ int checked_ctx(int raw, int max_ctx, int max_blocks, bool& bad) {
+  int lim = min(max_ctx, max_blocks * kPage);
+  if (raw < 0) { bad = true; return 0; }
+  if (raw > lim) { bad = true; return lim; }
+  return raw;
+}
+
+template <int D, int KV>
+struct DecodeTile {
+  // K fragments: 16-byte loads per MFMA row-half u.
+  static constexpr int KL = (KV == PKV_F32) ? D / 16 : (KV == PKV_I8 ? D / 64 : D / 32);
+  u32x4 k[2][KL];
+  // V^T fragments, one per 16-row block of d.
+  u32x4 v[D / 16][(KV == PKV_F32) ? 2 : 1];
+  u32x2 v8[D / 16];
+  f32x4 ks[2], vs[2];
+};
+
+template <int D, int KV>
+__device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs& a, int g,
+                                          int pa, int pb, int lane) {
+  const int r = lane & 15, kg = lane >> 4;
+  const int page_k = (r < 8) ? pa : pb;
+  const int rows_tok = 8 * ((r >> 2) & 1) + (r & 3);  // + 4*u
+  constexpr int ES = (KV == PKV_F32) ? 4 : (KV == PKV_I8 ? 1 : 2);
+  const char* kbase = static_cast<const char*>(a.k_cache) +
+                      ((long)page_k * a.hkv + g) * (long)(kPage * D) * ES;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const char* row = kbase + (long)(rows_tok + 4 * u) * D * ES;
+#pragma unroll
+    for (int s = 0; s < DecodeTile<D, KV>::KL; ++s) {
+      int d0;
+      if constexpr (KV == PKV_F32) d0 = 16 * s + 4 * kg;
+      else if constexpr (KV == PKV_I8) d0 = 64 * s + 16 * kg;
+      else d0 = 32 * s + 8 * kg;
+      t.k[u][s] = *reinterpret_cast<const u32x4*>(row + (long)d0 * ES);
+    }
+  }
+  const int page_v = (kg < 2) ? pa : pb;
+  const char* vbase = static_cast<const char*>(a.v_cache) +
+                      ((long)page_v * a.hkv + g) * (long)(D * kPage) * ES;
+#pragma unroll
+  for (int blk = 0; blk < D / 16; ++blk) {
+    const char* p = vbase + ((long)(16 * blk + r) * kPage + 8 * (kg & 1)) * ES;
+    if constexpr (KV == PKV_I8) {
+      t.v8[blk] = *reinterpret_cast<const u32x2*>(p);
+    } else if constexpr (KV == PKV_F32) {
+      t.v[blk][0] = *reinterpret_cast<const u32x4*>(p);
+      t.v[blk][1] = *reinterpret_cast<const u32x4*>(p + 16);
+    } else {
+      t.v[blk][0] = *reinterpret_cast<const u32x4*>(p);
+    }
+  }
+  if constexpr (KV == PKV_I8) {
+    // scales of the 8 tokens 8*kg..8*kg+7 this lane holds scores for
+    const long sidx = ((long)page_v * a.hkv + g) * kPage + 8 * (kg & 1);
+    t.ks[0] = *reinterpret_cast<const f32x4*>(a.k_scales + sidx);
+    t.ks[1] = *reinterpret_cast<const f32x4*>(a.k_scales + sidx + 4);
+    t.vs[0] = *reinterpret_cast<const f32x4*>(a.v_scales + sidx);
+    t.vs[1] = *reinterpret_cast<const f32x4*>(a.v_scales + sidx + 4);
+  }
+}
+
+template <int D, int KV>
+__global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) {
+  constexpr bool kF32 = (KV == PKV_F32);
+  constexpr bool kI8 = (KV == PKV_I8);
+  constexpr bool kBF16 = (KV == PKV_BF16);
+  using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
+  constexpr int NSTEP = kF32 ? D / 4 : D / 32;    // QK MFMA k-steps
+  constexpr int NBLK = D / 16;
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y / a.head_tiles;
+  const int ht = blockIdx.y % a.head_tiles;
+  const int b = blockIdx.z;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+
+  bool bad = false;
+  const int ctx = checked_ctx(a.context_lens[b], a.max_context_len, a.max_blocks, bad);
+  const int ntiles = (ctx + 31) >> 5;
+  const int nsplit_b = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  if (split >= (nsplit_b > 0 ? nsplit_b : 1)) return;
+  const int tile_begin = split * a.tiles_per_split;
+  const int tile_end = min(ntiles, tile_begin + a.tiles_per_split);
+  const int npages = (ctx + kPage - 1) / kPage;
+
+  const int h0 = g * a.group + ht * 16;
+  const int nh = min(16, a.group - ht * 16);
+
+  // ---- query fragments (B operand: column c = head h0 + c)
+  float qf[kF32 ? NSTEP : 1];
+  H8 qhi[kF32 ? 1 : NSTEP], qlo[kF32 ? 1 : NSTEP];
+  {
+    const long qrow = ((long)b * a.hq + h0 + c) * D;
+    const bool live = c < nh;
+    if constexpr (kF32) {
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        int d = 16 * (s >> 2) + 4 * j + (s & 3);
+        qf[s] = live ? load_as_f32(a.q, qrow + d, a.q_dtype) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        int d0 = kI8 ? (64 * (s >> 1) + 16 * j + 8 * (s & 1)) : (32 * s + 8 * j);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? load_as_f32(a.q, qrow + d0 + e, a.q_dtype) : 0.f;
+        if constexpr (kBF16) {
+          auto sp = split_bf16(x);
+          qhi[s] = sp.hi;
+          qlo[s] = sp.lo;
+        } else {
+          auto sp = split_f16(x);
+          qhi[s] = sp.hi;
+          qlo[s] = sp.lo;
+        }
+      }
+    }
+  }
+
+  f32x4 acc[NBLK];
+#pragma unroll
+  for (int i = 0; i < NBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+
+  const int32_t* bt = a.block_tables + (long)b * a.max_blocks;
+  auto page_of = [&](int idx) -> int {
+    int p = bt[idx];
+    if ((unsigned)p >= (unsigned)a.num_pages) { bad = true; p = 0; }
+    return p;
+  };
+
+  // Tiles are double-buffered in registers (the next tile's loads are in
+  // flight while this one computes) except for fp32 KV at d=128, whose
+  // tile alone takes 128 VGPRs.
+  constexpr bool kPrefetch = !(kF32 && D == 128);
+  DecodeTile<D, KV> cur, nxt;
+  auto load_at = [&](DecodeTile<D, KV>& dst, int tt) {
+    int pa = page_of(2 * tt);
+    int pb = (2 * tt + 1 < npages) ? page_of(2 * tt + 1) : pa;
+    load_tile<D, KV>(dst, a, g, pa, pb, lane);
+  };
+  int t = tile_begin + wave;
+  if (kPrefetch && t < tile_end) load_at(cur, t);
+  for (; t < tile_end; t += kDecodeWaves) {
+    if constexpr (kPrefetch) {
+      const int tn = t + kDecodeWaves;
+      if (tn < tile_end) load_at(nxt, tn);
+    } else {
+      load_at(cur, t);
+    }
+
+    // ---- S^T = K * Q^T for the 32 tile tokens
+    f32x4 s2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kF32) {
+#pragma unroll
+        for (int s4 = 0; s4 < D / 16; ++s4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc = mfma16x16x4(__uint_as_float(cur.k[u][s4][e]), qf[4 * s4 + e], sacc);
+        }
+      } else if constexpr (kI8) {
+#pragma unroll
+        for (int s2i = 0; s2i < D / 64; ++s2i) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            f16x8 kf;
+            i8x8_to_f16x8(u32x2{cur.k[u][s2i][2 * h], cur.k[u][s2i][2 * h + 1]}, kf);
+            sacc = mfma16x16x32(kf, qhi[2 * s2i + h], sacc);
+            sacc = mfma16x16x32(kf, qlo[2 * s2i + h], sacc);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+          H8 kf = __builtin_bit_cast(H8, cur.k[u][s]);
+          sacc = mfma16x16x32(kf, qhi[s], sacc);
+          sacc = mfma16x16x32(kf, qlo[s], sacc);
+        }
+      }
+      s2[u] = sacc;
+    }
+
+    // ---- scores of head c for tile tokens 8j + e, e = 4u + i
+    const int tok0 = 32 * t + 8 * j;
+    float sc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = s2[e >> 2][e & 3] * a.scale_log2;
+      if constexpr (kI8) x *= cur.ks[e >> 2][e & 3];
+      sc[e] = (tok0 + e < ctx) ? x : -INFINITY;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
+    mt = wave_max_xor_16_32(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float p[8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
+      lsum += p[e];
+    }
+    l_part = l_part * alpha + lsum;
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) acc[i] *= alpha;
+
+    const bool partial = (32 * t + 32 > ctx);
+    // ---- O^T += V^T * P^T
+    if constexpr (kF32) {
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float v = __uint_as_float(cur.v[blk][e >> 2][e & 3]);
+          if (partial && tok0 + e >= ctx) v = 0.f;
+          acc[blk] = mfma16x16x4(v, p[e], acc[blk]);
+        }
+      }
+    } else {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = p[e];
+        if constexpr (kI8) x = (tok0 + e < ctx) ? x * cur.vs[e >> 2][e & 3] : 0.f;
+        pv[e] = x;
+      }
+      H8 phi, plo;
+      if constexpr (kBF16) {
+        auto sp = split_bf16(pv);
+        phi = sp.hi;
+        plo = sp.lo;
+      } else {
+        auto sp = split_f16(pv);
+        phi = sp.hi;
+        plo = sp.lo;
+      }
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        H8 vf;
+        if constexpr (kI8) {
+          f16x8 tmp;
+          i8x8_to_f16x8(cur.v8[blk], tmp);
+          vf = tmp;
+        } else {
+          u32x4 w = cur.v[blk][0];
+          if (partial) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              if (tok0 + e >= ctx) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
+          }
+          vf = __builtin_bit_cast(H8, w);
+        }
+        acc[blk] = mfma16x16x32(vf, phi, acc[blk]);
+        acc[blk] = mfma16x16x32(vf, plo, acc[blk]);
+      }
+    }
+    if constexpr (kPrefetch) cur = nxt;
+  }
+  const float l_run = wave_sum_xor_16_32(l_part);
+
+  // ---- merge the four waves in LDS
+  __shared__ float s_m[kDecodeWaves][16];
+  __shared__ float s_l[kDecodeWaves][16];
+  __shared__ float s_o[kDecodeWaves][16][D + 1];
+  __shared__ int s_bad;
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  if (bad) atomicOr(&s_bad, 1);
+  if (j == 0) {
+    s_m[wave][c] = m_run;
+    s_l[wave][c] = l_run;
+  }
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[wave][c][16 * blk + 4 * j + i] = acc[blk][i];
+  }
+  __syncthreads();
+  const bool any_bad = s_bad != 0;
+  const bool direct = nsplit_b <= 1;
+  for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
+    const int hc = idx / D, d = idx - hc * D;
+    float M = s_m[0][hc];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][hc]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        float f = __builtin_amdgcn_exp2f(s_m[w][hc] - M);
+        num += s_o[w][hc][d] * f;
+        den += s_l[w][hc] * f;
+      }
+    }
+    float val = den > 0.f ? num / den : 0.f;
+    if (any_bad) val = NAN;
+    const long row = (long)b * a.hq + h0 + hc;
+    if (direct) {
+      store_from_f32(a.out, row * D + d, a.out_dtype, val);
+    } else {
+      const long prow = row * a.nsplits + split;
+      a.part_o[prow * D + d] = val;
+      if (d == 0) a.part_lse[prow] = any_bad ? NAN : (den > 0.f ? M + log2f(den) : -INFINITY);
+    }
+  }
+}
+
+// Log-sum-exp merge of the split partials of one (sequence, query head).
+template <int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  bool bad = false;
+  const int ctx = checked_ctx(a.context_lens[b], a.max_context_len, a.max_blocks, bad);
+  const int ntiles = (ctx + 31) >> 5;
+  const int ns = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  if (ns <= 1) return;
+  const long row = (long)b * a.hq + h;
+  const float* lse = a.part_lse + row * a.nsplits;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[s]);
+  for (int d = threadIdx.x; d < D; d += 64) {
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < ns; ++s) {
+        float w = __builtin_amdgcn_exp2f(lse[s] - M);
+        num += a.part_o[(row * a.nsplits + s) * D + d] * w;
+        den += w;
+      }
+    }
+    float val = den > 0.f ? num / den : 0.f;
+    if (bad) val = NAN;
+    store_from_f32(a.out, row * D + d, a.out_dtype, val);
+  }
+}
+
+template <int D, int KV>
+static void launch_decode(const DecodeArgs& a, pkv_stream_t stream) {
+  dim3 grid(a.nsplits, a.hkv * a.head_tiles, a.batch);
+  hipLaunchKernelGGL((decode_partition_kernel<D, KV>), grid, dim3(256), 0,
+                     (hipStream_t)stream, a);
+  if (a.nsplits > 1)
+    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.hq, a.batch), dim3(64), 0,
+                       (hipStream_t)stream, a);
+}
+
+template <int D>
+static void dispatch_kv(int kv, const DecodeArgs& a, pkv_stream_t stream) {
+  switch (kv) {
+    case PKV_F32: launch_decode<D, PKV_F32>(a, stream); break;
+    case PKV_BF16: launch_decode<D, PKV_BF16>(a, stream); break;
+    case PKV_F16: launch_decode<D, PKV_F16>(a, stream); break;
+    default: launch_decode<D, PKV_I8>(a, stream); break;
+  }
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
+                                                    int head_dim, int max_context_len) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      !head_dim_built(head_dim) || max_context_len < 0)
+    return 0;
+  DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+  return decode_workspace_bytes(batch, num_q_heads, head_dim, p);
+}
+
+extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache,
+                                 const void* v_cache, const float* k_scales,
+                                 const float* v_scales, int kv_dtype,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len, int batch,
+                                 int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                                 int num_pages, float scale, void* out, int out_dtype,
+                                 void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return PKV_ERR_INVALID_ARG;
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      num_pages <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE)
+    return PKV_ERR_INVALID_ARG;
+  if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
+    return PKV_ERR_INVALID_ARG;
+  if ((kv_dtype == PKV_I8) != (k_scales != nullptr) || (kv_dtype == PKV_I8) != (v_scales != nullptr))
+    return PKV_ERR_INVALID_ARG;
+  if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(block_tables) || !aligned16(context_lens) ||
+      (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)))
+    return PKV_ERR_MISALIGNED;
+
+  DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+  size_t need = decode_workspace_bytes(batch, num_q_heads, head_dim, p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace && !aligned16(workspace)) return PKV_ERR_MISALIGNED;
+
+  DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  size_t rows = (size_t)batch * num_q_heads * p.nsplits;
+  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               align_up(rows * head_dim * sizeof(float), 256))
+                    : nullptr;
+  a.q_dtype = q_dtype;
+  a.out_dtype = out_dtype;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.head_tiles = p.head_tiles;
+  a.num_pages = num_pages;
+  a.tiles_per_split = p.tiles_per_split;
+  a.nsplits = p.nsplits;
+  a.scale_log2 = scale * kLog2e;
+
+  clear_launch_error();
+  if (head_dim == 64) dispatch_kv<64>(kv_dtype, a, stream);
+  else dispatch_kv<128>(kv_dtype, a, stream);
+  return launch_status();
+}

@@ -1,0 +1,121 @@
+// Device-side helpers for the pkv kernels (gfx950 / CDNA4, wave64).
+//
+// Element conversions used by the append path are written on the bit
+// patterns so that they match the library's documented rounding exactly
+// (nearest-even bf16 with NaN kept quiet; IEEE fp16 via the hardware
+// convert, which rounds to nearest even and keeps subnormals).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = PKV_PAGE_SIZE;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Load element i of a row in dtype dt as float.
+__device__ __forceinline__ float load_as_f32(const void* base, long i, int dt) {
+  if (dt == PKV_F32) return static_cast<const float*>(base)[i];
+  if (dt == PKV_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+  return f16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+}
+
+__device__ __forceinline__ void store_from_f32(void* base, long i, int dt, float x) {
+  if (dt == PKV_F32) static_cast<float*>(base)[i] = x;
+  else if (dt == PKV_BF16) static_cast<uint16_t*>(base)[i] = (uint16_t)f32_to_bf16_bits(x);
+  else static_cast<uint16_t*>(base)[i] = (uint16_t)f32_to_f16_bits(x);
+}
+
+// ------------------------------------------------------------ MFMA
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Split fp32 values into a 16-bit head and a 16-bit remainder so that
+// head + remainder carries about 16 significant bits: the two MFMA products
+// then keep the fp32 operand's precision well below the output tolerance.
+template <typename V8>
+struct Split8 { V8 hi, lo; };
+
+__device__ __forceinline__ Split8<bf16x8> split_bf16(const float (&x)[8]) {
+  Split8<bf16x8> r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h = (__bf16)x[e];
+    r.hi[e] = h;
+    r.lo[e] = (__bf16)(x[e] - (float)h);
+  }
+  return r;
+}
+
+__device__ __forceinline__ Split8<f16x8> split_f16(const float (&x)[8]) {
+  Split8<f16x8> r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    _Float16 h = (_Float16)x[e];
+    r.hi[e] = h;
+    r.lo[e] = (_Float16)(x[e] - (float)h);
+  }
+  return r;
+}
+
+// int8 codes (4 per dword) -> fp16, exact.
+__device__ __forceinline__ void i8x8_to_f16x8(u32x2 w, f16x8& out) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int v = (int)(int8_t)((w[q] >> (8 * k)) & 0xffu);
+      out[4 * q + k] = (_Float16)(float)v;
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_max_xor_16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_xor_16_32(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace pkv

@@ -1,0 +1,125 @@
+"""The C ABI on the CPU: the library loads, exports every function pkv.h
+declares, and rejects bad arguments on the host before launching anything.
+
+The error-path calls pass fake device addresses; each call has an argument
+the host check rejects, so nothing is launched.  They run only where no GPU
+is visible, so a bug in the check order can never launch on fake pointers.
+"""
+import ctypes
+
+import pytest
+import torch
+
+from paged_kv_attention_10_amd import _lib
+
+NO_GPU = torch.cuda.device_count() == 0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert set(names) == {
+        "pkv_abi_version", "pkv_status_string", "paged_kv_append", "paged_attn_decode",
+        "paged_attn_decode_workspace_bytes", "paged_attn_prefill_chunk",
+        "paged_attn_prefill_workspace_bytes"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pkv_abi_version() == 1
+    for code in range(6):
+        assert lib.pkv_status_string(code).decode().startswith("PKV_")
+    assert lib.pkv_status_string(99).decode() == "PKV_ERR_UNKNOWN"
+
+
+def test_decode_workspace_query_is_pure(lib):
+    ws = lib.paged_attn_decode_workspace_bytes
+    assert ws(64, 12, 2, 128, 4096) == ws(64, 12, 2, 128, 4096) > 0
+    assert ws(384, 12, 12, 64, 1024) == 0          # contexts fit one partition
+    assert ws(0, 12, 2, 128, 4096) == 0            # invalid shapes -> 0
+    assert ws(4, 9, 2, 64, 200) == 0
+    assert ws(4, 9, 3, 96, 200) == 0
+    # more context never needs less workspace
+    sizes = [ws(16, 8, 1, 128, n) for n in (64, 512, 4096, 32768)]
+    assert sizes == sorted(sizes)
+    assert lib.paged_attn_prefill_workspace_bytes(8, 12, 2, 128, 512, 4096) == 0
+
+
+FAKE = 0x7f0000000000           # 16-byte aligned stand-in address, never dereferenced
+
+
+def _decode(lib, **over):
+    a = dict(q=FAKE, qd=0, k=FAKE, v=FAKE, ks=None, vs=None, kvd=1, bt=FAKE, mb=8, cl=FAKE,
+             mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125, out=FAKE, od=0,
+             ws=FAKE, wsb=1 << 20, st=None)
+    a.update(over)
+    return lib.paged_attn_decode(*a.values())
+
+
+def _prefill(lib, **over):
+    a = dict(q=FAKE, qd=1, k=FAKE, v=FAKE, ks=None, vs=None, kvd=1, bt=FAKE, mb=8, cl=FAKE,
+             cu=FAKE, T=64, mql=32, mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125,
+             out=FAKE, od=0, ws=None, wsb=0, st=None)
+    a.update(over)
+    return lib.paged_attn_prefill_chunk(*a.values())
+
+
+def _append(lib, **over):
+    a = dict(k=FAKE, v=FAKE, nd=0, slots=FAKE, T=4, kc=FAKE, vc=FAKE, ks=None, vs=None, cd=1,
+             np_=32, hkv=2, d=64, ps=16, st=None)
+    a.update(over)
+    return lib.paged_kv_append(*a.values())
+
+
+INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL = 1, 2, 3, 4
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, INVALID), ({"k": None}, INVALID), ({"out": None}, INVALID),
+    ({"bt": None}, INVALID), ({"cl": None}, INVALID),
+    ({"B": 0}, INVALID), ({"hq": 5}, INVALID), ({"hkv": 0}, INVALID), ({"np_": 0}, INVALID),
+    ({"mcl": 129}, INVALID), ({"mcl": -1}, INVALID), ({"mb": 0}, INVALID),
+    ({"qd": 3}, INVALID), ({"od": 7}, INVALID), ({"kvd": 4}, INVALID),
+    ({"kvd": 3}, INVALID),                                  # int8 KV without scales
+    ({"ks": FAKE, "vs": FAKE}, INVALID),                    # scales with a non-int8 KV
+    ({"ps": 8}, UNSUPPORTED), ({"d": 96}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED),
+    ({"q": FAKE + 4}, MISALIGNED), ({"v": FAKE + 8}, MISALIGNED), ({"out": FAKE + 2}, MISALIGNED),
+    ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "ws": None, "wsb": 0, "mb": 256}, WS_SMALL),
+    ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "wsb": 1024, "mb": 256}, WS_SMALL),
+])
+def test_decode_rejects(lib, over, code):
+    if code == WS_SMALL:
+        assert lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096) > 1024
+    assert _decode(lib, **over) == code
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, INVALID), ({"cu": None}, INVALID), ({"mql": 200}, INVALID),
+    ({"T": -1}, INVALID), ({"hq": 3}, INVALID), ({"mcl": 200}, INVALID),
+    ({"kvd": 0}, UNSUPPORTED), ({"kvd": 3, "ks": FAKE, "vs": FAKE}, UNSUPPORTED),
+    ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED), ({"cu": FAKE + 4}, MISALIGNED),
+    ({"od": 3}, INVALID),
+])
+def test_prefill_rejects(lib, over, code):
+    assert _prefill(lib, **over) == code
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    ({"T": -1}, INVALID), ({"nd": 3}, INVALID), ({"cd": 5}, INVALID), ({"cd": 3}, INVALID),
+    ({"np_": 0}, INVALID), ({"ps": 8}, UNSUPPORTED), ({"d": 32}, UNSUPPORTED),
+    ({"slots": None}, INVALID), ({"kc": FAKE + 4}, MISALIGNED), ({"slots": FAKE + 4}, MISALIGNED),
+])
+def test_append_rejects(lib, over, code):
+    assert _append(lib, **over) == code
+
+
+def test_append_zero_tokens_is_noop(lib):
+    assert _append(lib, T=0, k=None, v=None, slots=None) == 0

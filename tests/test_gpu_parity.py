@@ -1,0 +1,261 @@
+"""GPU parity: the HIP library against the fp64 oracle, through the C ABI.
+
+Tolerances (max abs error over every output element): 2e-5 for fp32 KV and
+1e-2 for bf16/fp16/int8 KV; append is compared byte for byte.  Unused pool
+slots are NaN on the GPU, so any read outside a sequence's context fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (TOL, TORCH_DT, config_case, gpu_to_np_bits, np_to_gpu, oracle_cache,
+                         poisoned_gpu_cache, q_exact_values, q_tensor, run_decode, run_prefill,
+                         say, small_decode, small_prefill, to_f64, used_slot_mask)
+from workloads import custom_workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_attention_10_amd as lib
+    return lib
+
+
+def _decode_check(pkv, w, cache, q_dtype="f32", out_dtype=torch.float32, tol=None, **kw):
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w, q_dtype)
+    out = run_decode(pkv, w, gc, q, out_dtype=out_dtype, **kw)
+    ref = oracle.ref_decode(q_exact_values(q), cache, w.block_tables, w.context_lens, w.scale,
+                            w.num_q_heads)
+    err = oracle.max_abs_err(to_f64(out), ref)
+    return err, (TOL[w.kv_dtype] if tol is None else tol)
+
+
+# ------------------------------------------------------------------ append
+@pytest.mark.parametrize("cache_dtype", ["f32", "bf16", "f16", "i8"])
+@pytest.mark.parametrize("new_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_append_bit_exact(pkv, cache_dtype, new_dtype, d):
+    say(f"append cache={cache_dtype} new={new_dtype} d={d}")
+    w = custom_workload(context_lens=[37, 16, 1, 90], num_q_heads=4, num_kv_heads=2, head_dim=d,
+                        kv_dtype=cache_dtype, num_pages=20, seed=40 + d)
+    k, v = w.k.copy(), w.v.copy()
+    # edge values: signed zeros, fp16 subnormals and overflow, bf16 ties, an all-zero vector
+    k[0, 0, :8] = [0.0, -0.0, 2.0**-25, 3 * 2.0**-25, 6e-8, 65520.0, 1.00390625, -1.01171875]
+    v[1, 1, :] = 0.0
+    k[2, 0, :4] = [np.float32(1e-40), -1e-41, 7e4, -1e5]
+    if cache_dtype == "i8":
+        # int8 quantization is specified for finite vectors only; keep the
+        # fp16-overflow values out of its input
+        k[0, 0, 5] = 60000.0
+        k[2, 0, 2:4] = [6e4, -5e4]
+    kt = torch.from_numpy(k).cuda().to(TORCH_DT[new_dtype])
+    vt = torch.from_numpy(v).cuda().to(TORCH_DT[new_dtype])
+    slots = w.slot_mapping.copy()
+    slots[[5, 40]] = -1
+    host = oracle.PagedCache(w.num_pages, 2, d, cache_dtype)
+    host.k.view(np.uint8)[:] = 0xA5
+    host.v.view(np.uint8)[:] = 0xA5
+    if cache_dtype == "i8":
+        host.k_scales.view(np.uint8)[:] = 0xA5
+        host.v_scales.view(np.uint8)[:] = 0xA5
+    gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
+    gks = np_to_gpu(host.k_scales) if cache_dtype == "i8" else None
+    gvs = np_to_gpu(host.v_scales) if cache_dtype == "i8" else None
+    pkv.paged_kv_append(kt, vt, torch.from_numpy(slots).cuda(), gk, gv, gks, gvs)
+    torch.cuda.synchronize()
+    oracle.ref_append(host, kt.float().cpu().numpy(), vt.float().cpu().numpy(), slots)
+    assert np.array_equal(gpu_to_np_bits(gk).view(np.uint8), host.k.view(np.uint8))
+    assert np.array_equal(gpu_to_np_bits(gv).view(np.uint8), host.v.view(np.uint8))
+    if cache_dtype == "i8":
+        assert np.array_equal(gks.cpu().numpy().view(np.uint32), host.k_scales.view(np.uint32))
+        assert np.array_equal(gvs.cpu().numpy().view(np.uint32), host.v_scales.view(np.uint32))
+
+
+def test_append_full_size_int8(pkv):
+    w, _ = config_case("C5")
+    say("append C5 full size int8")
+    host = oracle.PagedCache(w.num_pages, w.num_kv_heads, w.head_dim, "i8")
+    gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
+    gks, gvs = np_to_gpu(host.k_scales), np_to_gpu(host.v_scales)
+    pkv.paged_kv_append(torch.from_numpy(w.k).cuda(), torch.from_numpy(w.v).cuda(),
+                        torch.from_numpy(w.slot_mapping).cuda(), gk, gv, gks, gvs)
+    torch.cuda.synchronize()
+    oracle.ref_append(host, w.k, w.v, w.slot_mapping)
+    assert np.array_equal(gk.cpu().numpy(), host.k)
+    assert np.array_equal(gv.cpu().numpy(), host.v)
+    assert np.array_equal(gks.cpu().numpy().view(np.uint32), host.k_scales.view(np.uint32))
+    assert np.array_equal(gvs.cpu().numpy().view(np.uint32), host.v_scales.view(np.uint32))
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C5"])
+def test_decode_config_full_size(pkv, name):
+    w, cache = config_case(name)
+    say(f"decode {name} full size: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} kv={w.kv_dtype}")
+    err, tol = _decode_check(pkv, w, cache)
+    say(f"  max abs err {err:.3e} (tol {tol})")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "f16", "i8"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (9, 3), (8, 1), (32, 2)])
+def test_decode_small(pkv, kv, d, hq, hkv):
+    ctx = [1, 15, 16, 17, 31, 32, 33, 0, 100, 257, 700]
+    w = small_decode(ctx, hq, hkv, d, kv, seed=hq * 7 + d + len(kv))
+    say(f"decode small kv={kv} d={d} hq={hq} hkv={hkv}")
+    err, tol = _decode_check(pkv, w, oracle_cache(w))
+    assert err <= tol, err
+
+
+@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_decode_io_dtypes(pkv, q_dtype, out_dtype):
+    w = small_decode([5, 64, 300, 1000], 12, 2, 128, "bf16", seed=7)
+    say(f"decode io q={q_dtype} out={out_dtype}")
+    err, tol = _decode_check(pkv, w, oracle_cache(w), q_dtype=q_dtype, out_dtype=out_dtype)
+    assert err <= tol, err
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8"])
+def test_decode_split_counts_agree(pkv, kv):
+    """Raising max_context_len changes how contexts are split into
+    partitions (and how many partials the LSE reduce merges); the result
+    must stay within tolerance for every split."""
+    w = small_decode([3000, 17, 1500, 4096, 600], 8, 2, 64, kv, seed=9, table_width=512)
+    cache = oracle_cache(w)
+    for mcl in (4096, 5000, 8192):
+        say(f"decode split kv={kv} max_context_len={mcl}")
+        err, tol = _decode_check(pkv, w, cache, max_context_len=mcl)
+        assert err <= tol, (mcl, err)
+
+
+def test_decode_page_permutation_bit_exact(pkv):
+    w = small_decode([40, 300, 77], 6, 2, 128, "bf16", seed=3, num_pages=64)
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w)
+    out1 = run_decode(pkv, w, gc, q)
+    perm = np.random.Generator(np.random.PCG64(1)).permutation(w.num_pages)
+    inv = np.argsort(perm)
+    gc2 = dict(gc)
+    gc2["k"] = gc["k"][torch.from_numpy(perm).cuda()].contiguous()
+    gc2["v"] = gc["v"][torch.from_numpy(perm).cuda()].contiguous()
+    out2 = run_decode(pkv, w, gc2, q, block_tables=inv[w.block_tables].astype(np.int32))
+    assert torch.equal(out1, out2)
+
+
+def test_decode_bad_page_id_gives_nan(pkv):
+    w = small_decode([40, 50], 4, 2, 64, "f16", seed=5)
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    bt = w.block_tables.copy()
+    bt[1, 1] = w.num_pages + 100          # out of the pool
+    out = run_decode(pkv, w, gc, q_tensor(w), block_tables=bt)
+    o = out.cpu().numpy()
+    assert np.all(np.isnan(o[1])) and np.all(np.isfinite(o[0]))
+
+
+def test_decode_memory_stable(pkv):
+    w = small_decode([100, 2000, 50], 12, 2, 128, "bf16", seed=2)
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w)
+    run_decode(pkv, w, gc, q)
+    before = torch.cuda.memory_allocated()
+    for _ in range(5):
+        out = run_decode(pkv, w, gc, q)
+        del out
+    assert torch.cuda.memory_allocated() == before
+
+
+# ------------------------------------------------------------------ prefill
+def _prefill_check(pkv, w, cache, q_dtype="bf16", out_dtype=torch.float32):
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w, q_dtype)
+    out = run_prefill(pkv, w, gc, q, out_dtype=out_dtype)
+    ref = oracle.ref_prefill_chunk(q_exact_values(q), cache, w.block_tables, w.context_lens,
+                                   w.cu_q_lens, w.scale)
+    return oracle.max_abs_err(to_f64(out), ref)
+
+
+def test_prefill_config_full_size(pkv):
+    w, cache = config_case("C4")
+    say(f"prefill C4 full size: prefixes {w.meta['prefix_lens'].tolist()}")
+    err = _prefill_check(pkv, w, cache)
+    say(f"  max abs err {err:.3e}")
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (6, 2), (12, 2), (3, 1)])
+def test_prefill_small(pkv, kv, d, hq, hkv):
+    ctx = [16, 40, 17, 200, 33, 130]
+    ql = [16, 7, 17, 150, 1, 64]           # prefixes 0, 33, 0, 50, 32, 66
+    w = small_prefill(ctx, ql, hq, hkv, d, kv, seed=hq + d)
+    say(f"prefill small kv={kv} d={d} hq={hq} hkv={hkv}")
+    err = _prefill_check(pkv, w, oracle_cache(w), q_dtype=kv)
+    assert err <= 1e-2, err
+
+
+@pytest.mark.parametrize("q_dtype", ["f32", "f16"])
+def test_prefill_q_other_dtype(pkv, q_dtype):
+    w = small_prefill([300, 90], [100, 90], 6, 2, 128, "bf16", seed=8)
+    say(f"prefill bf16 KV with q={q_dtype}")
+    err = _prefill_check(pkv, w, oracle_cache(w), q_dtype=q_dtype)
+    assert err <= 1e-2, err
+
+
+def test_prefill_rows_match_decode(pkv):
+    """Chunk row i equals a decode over the first P+i+1 tokens."""
+    w = small_prefill([90], [40], 6, 2, 128, "bf16", seed=4)
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w, "bf16")
+    pre = run_prefill(pkv, w, gc, q)
+    P = 50
+    for i in (0, 13, 39):
+        wd = small_decode([P + i + 1], 6, 2, 128, "bf16", seed=4)
+        wd.block_tables = w.block_tables.copy()
+        wd.q = w.q[i:i + 1].copy()
+        dec = run_decode(pkv, wd, gc, q[i:i + 1].contiguous())
+        assert torch.max(torch.abs(dec[0] - pre[i])).item() <= 1e-2
+
+
+# ------------------------------------------------------------------ errors
+def test_error_codes_with_device_buffers(pkv):
+    w = small_decode([20], 4, 2, 64, "bf16", seed=1)
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w)
+    bt, cl = np_to_gpu(w.block_tables), np_to_gpu(w.context_lens)
+    lib = pkv.load_library()
+    import ctypes
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    out = torch.empty((1, 4, 64), device="cuda")
+
+    def call(**over):
+        args = dict(q=P(q), qd=0, k=P(gc["k"]), v=P(gc["v"]), ks=None, vs=None, kvd=1, bt=P(bt),
+                    mb=int(w.block_tables.shape[1]), cl=P(cl), mcl=20, B=1, hq=4, hkv=2, d=64,
+                    ps=16, np_=w.num_pages, sc=0.125, out=P(out), od=0, ws=None, wsb=0, st=None)
+        args.update(over)
+        return lib.paged_attn_decode(*args.values())
+
+    assert call() == 0
+    torch.cuda.synchronize()
+    assert call(q=None) == 1
+    assert call(hq=5) == 1
+    assert call(ps=8) == 2
+    assert call(d=96) == 2
+    assert call(kvd=3) == 1                       # int8 without scales
+    assert call(qd=3) == 1                        # int8 query
+    assert call(mcl=10000) == 1                   # beyond the block table
+    assert call(q=ctypes.c_void_p(q.data_ptr() + 4)) == 3
+    assert call(mcl=20, B=1, hq=4, hkv=2) == 0
+    torch.cuda.synchronize()
