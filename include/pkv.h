@@ -132,10 +132,12 @@ int paged_kv_append(const void* k_new, const void* v_new, int new_dtype,
  *   workspace      device scratch of at least
  *                  paged_attn_decode_workspace_bytes(...) bytes (may be NULL
  *                  when that is 0); its contents on entry do not matter.
+ *                  Calls that run concurrently must not share a workspace.
  *
  * Built for head_dim 64 and 128, page_size 16, any num_q_heads/num_kv_heads
- * ratio.  Long contexts are split into partitions whose softmax partials
- * are merged by a log-sum-exp reduction on the same stream.
+ * ratio, max_context_len up to 262144 (PKV_ERR_UNSUPPORTED beyond).  Long
+ * contexts are split into partitions whose softmax partials are merged with
+ * their log-sum-exp weights by a second kernel on the same stream.
  */
 int paged_attn_decode(const void* q, int q_dtype,
                       const void* k_cache, const void* v_cache,
@@ -148,7 +150,8 @@ int paged_attn_decode(const void* q, int q_dtype,
                       void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
 /* Workspace bytes paged_attn_decode needs for these shapes (0 when the
- * contexts fit one partition).  Pure host arithmetic; touches no device. */
+ * contexts fit one partition, or for invalid shapes).  Pure host
+ * arithmetic; touches no device. */
 size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
                                          int head_dim, int max_context_len);
 

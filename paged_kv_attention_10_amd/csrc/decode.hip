@@ -5,10 +5,18 @@
 //
 // Work split.  A workgroup of 4 waves owns one (sequence b, KV head g, tile
 // of up to 16 query heads, context split).  The context is walked in tiles
-// of 32 tokens (two pages); wave w takes tiles w, w+4, ... of its split and
-// keeps its own running max / sum / accumulator.  The four waves merge in
-// LDS; a sequence whose context needs several splits writes normalised
-// partials plus a log2-sum-exp per split, merged by decode_reduce_kernel.
+// of 32 tokens (two pages); each wave takes a contiguous quarter of its
+// split.  The page ids of that run are fetched with one vector load (lane i
+// holds the i-th page id) issued together with the context length and the
+// query, since the run's place in the block-table row depends only on the
+// split index; tiles then stream through a ring of register buffers, the
+// next tile's loads in flight while the current one computes.  Each wave
+// keeps its own running max / sum / accumulator; the four waves merge in
+// LDS.  A sequence whose context needs several splits writes normalised
+// partials and a log2-sum-exp per split, merged by decode_reduce_kernel on
+// the same stream (the kernel boundary makes the partials visible across
+// the XCDs' separate L2 caches, which an in-kernel merge would have to
+// write back and invalidate).
 //
 // MFMA mapping (16x16 tiles, wave64).  Scores are computed transposed,
 // S^T = K * Q^T: A = K (row = token), B = Q^T (column = query head of the
@@ -68,10 +76,20 @@ struct DecodeTile {
   static constexpr int KL = (KV == PKV_F32) ? D / 16 : (KV == PKV_I8 ? D / 64 : D / 32);
   u32x4 k[2][KL];
   // V^T fragments, one per 16-row block of d.
-  u32x4 v[D / 16][(KV == PKV_F32) ? 2 : 1];
-  u32x2 v8[D / 16];
+  u32x4 v[(KV == PKV_I8) ? 1 : D / 16][(KV == PKV_F32) ? 2 : 1];
+  u32x2 v8[(KV == PKV_I8) ? D / 16 : 1];
   f32x4 ks[2], vs[2];
 };
+
+// Register ring depth: tiles in flight per wave, sized so the ring, the
+// query fragments and the accumulators stay within the VGPR budget.
+template <int D, int KV>
+constexpr int ring_depth() {
+#ifdef PKV_DECODE_RING
+  if (!(KV == PKV_F32 && D == 128)) return PKV_DECODE_RING;
+#endif
+  return (KV == PKV_F32 && D == 128) ? 1 : 2;
+}
 
 template <int D, int KV>
 __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs& a, int g,
@@ -119,14 +137,19 @@ __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs
   }
 }
 
+#ifndef PKV_DECODE_MIN_WAVES
+#define PKV_DECODE_MIN_WAVES 2
+#endif
+
 template <int D, int KV>
-__global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_kernel(DecodeArgs a) {
   constexpr bool kF32 = (KV == PKV_F32);
   constexpr bool kI8 = (KV == PKV_I8);
   constexpr bool kBF16 = (KV == PKV_BF16);
   using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
   constexpr int NSTEP = kF32 ? D / 4 : D / 32;    // QK MFMA k-steps
   constexpr int NBLK = D / 16;
+  constexpr int R = ring_depth<D, KV>();
 
   const int split = blockIdx.x;
   const int g = blockIdx.y / a.head_tiles;
@@ -136,20 +159,18 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int j = lane >> 4;
-
-  bool bad = false;
-  const int ctx = checked_ctx(a.context_lens[b], a.max_context_len, a.max_blocks, bad);
-  const int ntiles = (ctx + 31) >> 5;
-  const int nsplit_b = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  if (split >= (nsplit_b > 0 ? nsplit_b : 1)) return;
-  const int tile_begin = split * a.tiles_per_split;
-  const int tile_end = min(ntiles, tile_begin + a.tiles_per_split);
-  const int npages = (ctx + kPage - 1) / kPage;
-
   const int h0 = g * a.group + ht * 16;
   const int nh = min(16, a.group - ht * 16);
 
-  // ---- query fragments (B operand: column c = head h0 + c)
+  // ---- first round trip: context length, this wave's page ids, the query
+  const int raw_ctx = a.context_lens[b];
+  const int tpw = a.tiles_per_split / kDecodeWaves;
+  const int wt0 = split * a.tiles_per_split + wave * tpw;   // first tile of the wave
+  const int wp0 = 2 * wt0;                                  // its first page
+  int pid = 0;
+  if (lane < 2 * tpw && wp0 + lane < a.max_blocks)
+    pid = a.block_tables[(long)b * a.max_blocks + wp0 + lane];
+
   float qf[kF32 ? NSTEP : 1];
   H8 qhi[kF32 ? 1 : NSTEP], qlo[kF32 ? 1 : NSTEP];
   {
@@ -181,39 +202,29 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
     }
   }
 
+  bool bad = false;
+  const int ctx = checked_ctx(raw_ctx, a.max_context_len, a.max_blocks, bad);
+  const int ntiles = (ctx + 31) >> 5;
+  const int nsplit_b = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  if (split >= (nsplit_b > 0 ? nsplit_b : 1)) return;
+  const int npages = (ctx + kPage - 1) / kPage;
+  const int ntw = max(0, min(ntiles - wt0, tpw));
+  const int npw = max(0, min(npages - wp0, 2 * ntw));
+  if (lane < npw && (unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
+
   f32x4 acc[NBLK];
 #pragma unroll
   for (int i = 0; i < NBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  const int32_t* bt = a.block_tables + (long)b * a.max_blocks;
-  auto page_of = [&](int idx) -> int {
-    int p = bt[idx];
-    if ((unsigned)p >= (unsigned)a.num_pages) { bad = true; p = 0; }
-    return p;
-  };
-
-  // Tiles are double-buffered in registers (the next tile's loads are in
-  // flight while this one computes) except for fp32 KV at d=128, whose
-  // tile alone takes 128 VGPRs.
-  constexpr bool kPrefetch = !(kF32 && D == 128);
-  DecodeTile<D, KV> cur, nxt;
-  auto load_at = [&](DecodeTile<D, KV>& dst, int tt) {
-    int pa = page_of(2 * tt);
-    int pb = (2 * tt + 1 < npages) ? page_of(2 * tt + 1) : pa;
+  auto issue = [&](DecodeTile<D, KV>& dst, int li) {
+    const int pa = __builtin_amdgcn_readlane(pid, 2 * li);
+    const int pb = (2 * li + 1 < npw) ? __builtin_amdgcn_readlane(pid, 2 * li + 1) : pa;
     load_tile<D, KV>(dst, a, g, pa, pb, lane);
   };
-  int t = tile_begin + wave;
-  if (kPrefetch && t < tile_end) load_at(cur, t);
-  for (; t < tile_end; t += kDecodeWaves) {
-    if constexpr (kPrefetch) {
-      const int tn = t + kDecodeWaves;
-      if (tn < tile_end) load_at(nxt, tn);
-    } else {
-      load_at(cur, t);
-    }
 
+  auto compute = [&](const DecodeTile<D, KV>& cur, int li) {
     // ---- S^T = K * Q^T for the 32 tile tokens
     f32x4 s2[2];
 #pragma unroll
@@ -249,6 +260,7 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
     }
 
     // ---- scores of head c for tile tokens 8j + e, e = 4u + i
+    const int t = wt0 + li;
     const int tok0 = 32 * t + 8 * j;
     float sc[8];
 #pragma unroll
@@ -314,20 +326,35 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
           i8x8_to_f16x8(cur.v8[blk], tmp);
           vf = tmp;
         } else {
-          u32x4 w = cur.v[blk][0];
+          u32x4 wv = cur.v[blk][0];
           if (partial) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              if (tok0 + e >= ctx) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+              if (tok0 + e >= ctx) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
             }
           }
-          vf = __builtin_bit_cast(H8, w);
+          vf = __builtin_bit_cast(H8, wv);
         }
         acc[blk] = mfma16x16x32(vf, phi, acc[blk]);
         acc[blk] = mfma16x16x32(vf, plo, acc[blk]);
       }
     }
-    if constexpr (kPrefetch) cur = nxt;
+  };
+
+  // ---- stream the wave's tiles through the register ring
+  DecodeTile<D, KV> ring[R];
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r)
+    if (r < ntw) issue(ring[r], r);
+  for (int i0 = 0; i0 < ntw; i0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = i0 + r;
+      if (i < ntw) {
+        if (i + R - 1 < ntw) issue(ring[(r + R - 1) % R], i + R - 1);
+        compute(ring[r], i);
+      }
+    }
   }
   const float l_run = wave_sum_xor_16_32(l_part);
 
@@ -378,39 +405,68 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
   }
 }
 
-// Log-sum-exp merge of the split partials of one (sequence, query head).
+// Log-sum-exp merge of the split partials of one (sequence, query head):
+// out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
+// One wave per row; the context length, every split's lse and every
+// partial element this lane needs are loaded together, so the merge costs
+// one memory round trip.  Rows whose sequence fit one split were written by
+// the partition kernel and are skipped.
 template <int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const long row = (long)b * a.hq + h;
+  const int S = a.nsplits;                       // <= kDecodeMaxSplits
+  const int raw_ctx = a.context_lens[b];
+  const float lse_l = lane < S ? a.part_lse[row * S + lane] : -INFINITY;
+  float o[kDecodeMaxSplits][PER];
+#pragma unroll
+  for (int s = 0; s < kDecodeMaxSplits; ++s) {
+    if (s < S) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[s][e] = a.part_o[(row * S + s) * D + lane + 64 * e];
+    }
+  }
   bool bad = false;
-  const int ctx = checked_ctx(a.context_lens[b], a.max_context_len, a.max_blocks, bad);
+  const int ctx = checked_ctx(raw_ctx, a.max_context_len, a.max_blocks, bad);
   const int ntiles = (ctx + 31) >> 5;
   const int ns = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
   if (ns <= 1) return;
-  const long row = (long)b * a.hq + h;
-  const float* lse = a.part_lse + row * a.nsplits;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[s]);
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < ns; ++s) {
-        float w = __builtin_amdgcn_exp2f(lse[s] - M);
-        num += a.part_o[(row * a.nsplits + s) * D + d] * w;
-        den += w;
-      }
+  const float mine = lane < ns ? lse_l : -INFINITY;
+  float M = mine;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+  const float w_l = (M == -INFINITY || lane >= ns) ? 0.f : __builtin_amdgcn_exp2f(mine - M);
+  float den = w_l;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m);
+  // a NaN partial (a split that met a bad page id) poisons the row
+  const bool nan_in = __any(mine != mine);
+  float num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kDecodeMaxSplits; ++s) {
+    if (s < ns) {
+      const float w = __shfl(w_l, s);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] += o[s][e] * w;
     }
-    float val = den > 0.f ? num / den : 0.f;
-    if (bad) val = NAN;
-    store_from_f32(a.out, row * D + d, a.out_dtype, val);
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    float val = den > 0.f ? num[e] / den : 0.f;
+    if (bad || nan_in) val = NAN;
+    store_from_f32(a.out, row * D + lane + 64 * e, a.out_dtype, val);
   }
 }
 
 template <int D, int KV>
 static void launch_decode(const DecodeArgs& a, pkv_stream_t stream) {
   dim3 grid(a.nsplits, a.hkv * a.head_tiles, a.batch);
-  hipLaunchKernelGGL((decode_partition_kernel<D, KV>), grid, dim3(256), 0,
+  hipLaunchKernelGGL((decode_partition_kernel<D, KV>), grid, dim3(64 * kDecodeWaves), 0,
                      (hipStream_t)stream, a);
   if (a.nsplits > 1)
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.hq, a.batch), dim3(64), 0,
@@ -434,10 +490,10 @@ using namespace pkv;
 extern "C" size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
                                                     int head_dim, int max_context_len) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
-      !head_dim_built(head_dim) || max_context_len < 0)
+      !head_dim_built(head_dim) || max_context_len < 0 || (long)max_context_len > kDecodeMaxContext)
     return 0;
   DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
-  return decode_workspace_bytes(batch, num_q_heads, head_dim, p);
+  return decode_workspace_layout(batch, num_q_heads, head_dim, p).total;
 }
 
 extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache,
@@ -452,21 +508,23 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
     return PKV_ERR_INVALID_ARG;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
       num_pages <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE)
+      (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE || batch > 65535)
     return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
     return PKV_ERR_INVALID_ARG;
   if ((kv_dtype == PKV_I8) != (k_scales != nullptr) || (kv_dtype == PKV_I8) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
-  if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim) ||
+      (long)max_context_len > kDecodeMaxContext)
+    return PKV_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(block_tables) || !aligned16(context_lens) ||
       (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)))
     return PKV_ERR_MISALIGNED;
 
   DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
-  size_t need = decode_workspace_bytes(batch, num_q_heads, head_dim, p);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, head_dim, p);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (workspace && !aligned16(workspace)) return PKV_ERR_MISALIGNED;
 
   DecodeArgs a;
@@ -478,11 +536,9 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  size_t rows = (size_t)batch * num_q_heads * p.nsplits;
-  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
-  a.part_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                               align_up(rows * head_dim * sizeof(float), 256))
-                    : nullptr;
+  char* wsb = static_cast<char*>(workspace);
+  a.part_o = ws.total ? reinterpret_cast<float*>(wsb + ws.part_o_offset) : nullptr;
+  a.part_lse = ws.total ? reinterpret_cast<float*>(wsb + ws.part_lse_offset) : nullptr;
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
   a.max_blocks = max_blocks_per_seq;

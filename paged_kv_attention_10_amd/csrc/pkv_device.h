@@ -94,15 +94,24 @@ __device__ __forceinline__ Split8<f16x8> split_f16(const float (&x)[8]) {
   return r;
 }
 
-// int8 codes (4 per dword) -> fp16, exact.
+// int8 codes (4 per dword) -> fp16, exact.  Flipping the sign bit turns a
+// code x into the byte x + 128; v_perm places each such byte under the fp16
+// exponent of 1024 (bits 0x64xx), which reads as 1024 + x + 128, and one
+// packed fp16 subtraction of 1152 leaves x.  Every step is exact (all
+// values are integers below 2048).
 __device__ __forceinline__ void i8x8_to_f16x8(u32x2 w, f16x8& out) {
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      int v = (int)(int8_t)((w[q] >> (8 * k)) & 0xffu);
-      out[4 * q + k] = (_Float16)(float)v;
-    }
+    const uint32_t u = w[q] ^ 0x80808080u;
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // bytes 0, 1
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // bytes 2, 3
+    const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
+    const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
+    out[4 * q + 0] = a[0];
+    out[4 * q + 1] = a[1];
+    out[4 * q + 2] = b[0];
+    out[4 * q + 3] = b[1];
   }
 }
 

@@ -20,9 +20,9 @@ inline int launch_status() { return hipGetLastError() == hipSuccess ? PKV_OK : P
 
 // How a decode call is cut into work: contexts are processed in tiles of 32
 // tokens (two pages); a workgroup of 4 waves owns `tiles_per_split` tiles of
-// one (sequence, KV head, head tile); `nsplits` workgroups cover the
-// longest context.  Pure function of the shapes, so the workspace query and
-// the launch agree.
+// one (sequence, KV head, head tile), each wave a contiguous quarter of them;
+// `nsplits` workgroups cover the longest context.  A pure function of the
+// shapes, so the workspace query and the launch agree.
 struct DecodePlan {
   int head_tiles;
   int tiles_per_split;
@@ -31,9 +31,20 @@ struct DecodePlan {
 
 constexpr int kDecodeTileTokens = 32;
 constexpr int kDecodeWaves = 4;
-// Aim for about this many workgroups per call: four per CU on a 256-CU
-// MI355X, so short and long sequences interleave across the chip.
-constexpr long kDecodeTargetWorkgroups = 1024;
+// A wave's page ids are held one per lane, so a wave takes at most 32 tiles.
+constexpr int kDecodeMaxTilesPerSplit = 32 * kDecodeWaves;
+// The merge kernel holds one split per lane.
+constexpr int kDecodeMaxSplits = 64;
+// Longest context a decode call takes.
+constexpr long kDecodeMaxContext = (long)kDecodeMaxSplits * kDecodeMaxTilesPerSplit * kDecodeTileTokens;
+// Aim for about this many workgroups per call: one per CU of a 256-CU
+// MI355X.  Fewer, longer splits measured faster than more, shorter ones:
+// every split pays a few dependent memory round trips before its first
+// tile streams and leaves a partial for the merge.
+#ifndef PKV_DECODE_TARGET_WORKGROUPS
+#define PKV_DECODE_TARGET_WORKGROUPS 256
+#endif
+constexpr long kDecodeTargetWorkgroups = PKV_DECODE_TARGET_WORKGROUPS;
 
 inline DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len) {
   DecodePlan p;
@@ -44,19 +55,32 @@ inline DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int 
   long want = (kDecodeTargetWorkgroups + units - 1) / units;
   if (want < 1) want = 1;
   int tps = ceil_div(tiles_max, want);
-  if (tps < kDecodeWaves) tps = kDecodeWaves;
   tps = ceil_div(tps, kDecodeWaves) * kDecodeWaves;
+  if (tps < kDecodeWaves) tps = kDecodeWaves;
+  if (tps > kDecodeMaxTilesPerSplit) tps = kDecodeMaxTilesPerSplit;
   p.tiles_per_split = tps;
-  p.nsplits = ceil_div(tiles_max, tps);
+  p.nsplits = ceil_div(tiles_max, tps);   // <= kDecodeMaxSplits for contexts <= kDecodeMaxContext
   return p;
 }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, const DecodePlan& p) {
-  if (p.nsplits <= 1) return 0;
+// Workspace of a split decode: normalised partial outputs and their
+// log2-sum-exp, [batch][num_q_heads][nsplits] rows.  Contents on entry do
+// not matter.
+struct DecodeWorkspace {
+  size_t part_o_offset, part_lse_offset, total;
+};
+
+inline DecodeWorkspace decode_workspace_layout(int batch, int num_q_heads, int head_dim,
+                                               const DecodePlan& p) {
+  DecodeWorkspace w = {0, 0, 0};
+  if (p.nsplits <= 1) return w;
   size_t rows = (size_t)batch * num_q_heads * p.nsplits;
-  return align_up(rows * head_dim * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+  w.part_o_offset = 0;
+  w.part_lse_offset = align_up(rows * head_dim * sizeof(float), 256);
+  w.total = w.part_lse_offset + align_up(rows * sizeof(float), 256);
+  return w;
 }
 
 }  // namespace pkv

@@ -89,6 +89,7 @@ INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL = 1, 2, 3, 4
     ({"kvd": 3}, INVALID),                                  # int8 KV without scales
     ({"ks": FAKE, "vs": FAKE}, INVALID),                    # scales with a non-int8 KV
     ({"ps": 8}, UNSUPPORTED), ({"d": 96}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED),
+    ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest context built
     ({"q": FAKE + 4}, MISALIGNED), ({"v": FAKE + 8}, MISALIGNED), ({"out": FAKE + 2}, MISALIGNED),
     ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "ws": None, "wsb": 0, "mb": 256}, WS_SMALL),
     ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "wsb": 1024, "mb": 256}, WS_SMALL),

@@ -239,6 +239,8 @@ def test_error_codes_with_device_buffers(pkv):
     import ctypes
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     out = torch.empty((1, 4, 64), device="cuda")
+    nws = pkv.paged_attn_decode_workspace_bytes(1, 4, 2, 64, 20)
+    assert nws == 0                       # one partition: no workspace
 
     def call(**over):
         args = dict(q=P(q), qd=0, k=P(gc["k"]), v=P(gc["v"]), ks=None, vs=None, kvd=1, bt=P(bt),
