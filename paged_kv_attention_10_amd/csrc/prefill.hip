@@ -7,18 +7,27 @@
 // Rows.  The query rows of one (sequence, KV head) are the chunk positions
 // times the G query heads that share the KV head, flattened head-fastest:
 // row r -> position r / G, head g*G + r % G.  A workgroup of 4 waves owns 128
-// consecutive rows, a wave 32; every wave walks the key tiles its rows need
-// (32 keys = two pages per tile), so the G heads of a position reuse each
-// K/V fragment.
+// consecutive rows, a wave 32.  The workgroup walks the key tiles its rows
+// need (32 keys = two pages per tile); each tile's K and V^T are loaded once,
+// cooperatively, into LDS (double-buffered, rows padded so the fragment
+// reads are free of bank conflicts) and read by all four waves, so the G
+// heads of a position and the 32-row blocks of the chunk share every load.
+// Page ids are fetched two tiles ahead; tiles past a wave's causal limit
+// skip its math.
 //
 // MFMA mapping (32x32x16, wave64).  S^T = K * Q^T: A = K (row = key),
-// B = Q^T (column = query row).  The A-operand row rho loads key
+// B = Q^T (column = query row).  The A-operand row rho reads key
 // 16*(rho/16) + 8*((rho/4)&1) + 4*((rho/8)&1) + rho%4, which makes lane
 // (c + 32*h) hold, for query row c, the scores of keys 8h..8h+7 of the first
 // page (registers 0-7) and of the second page (registers 8-15): the
 // B-operand layout of O^T = V^T * P^T with no data movement.  The V page is
-// stored token-innermost, so each V^T A-operand load is a contiguous 8-key
+// stored token-innermost, so each V^T A-operand read is a contiguous 8-key
 // run.  The causal mask is applied only to tiles that cross a row's limit.
+//
+// Softmax.  exp2 of log2e-prescaled scores with a lazily updated running
+// max: the accumulator is rescaled only when a row's max grows by more than
+// 2^8 (the stale max cancels in the final normalisation, and probabilities
+// stay below 256).
 //
 // Precision: q and K/V in the cache's 16-bit type (an fp32 or other-typed
 // q is split into head + remainder and multiplied twice), P rounded to the
@@ -59,18 +68,39 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+// LDS tile layout (per stage): K as 32 key rows of D elements padded by 16
+// bytes; V^T as D rows of 32 keys padded by 16 bytes.
+template <int D>
+struct PrefillLds {
+  static constexpr int kRow = D * 2 + 16;
+  static constexpr int vRow = 32 * 2 + 16;
+  static constexpr int vOff = 32 * kRow;
+  static constexpr int stage = vOff + D * vRow;
+  static constexpr int chunks = D / 64;   // 16-byte chunks per thread, each of K and V
+};
+
+constexpr float kLazyRescale = 8.0f;
+
 template <int D, int KV, bool QSPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   constexpr bool kBF16 = (KV == PKV_BF16);
   using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
+  using L = PrefillLds<D>;
   constexpr int NSTEP = D / 16;  // QK k-steps of 16
   constexpr int NDB = D / 32;    // 32-row blocks of d for PV
+  __shared__ __attribute__((aligned(16))) char lds[2][L::stage];
 
+#ifdef PKV_PREFILL_ROWBLOCK_FASTEST
+  const int rb = a.nrowblocks - 1 - (int)blockIdx.x;
+  const int b = blockIdx.z;
+#else
   const int b = blockIdx.x;
-  const int g = blockIdx.y;
   const int rb = a.nrowblocks - 1 - (int)blockIdx.z;  // heavier (later) rows first
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+#endif
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int col = lane & 31;
   const int hh = lane >> 5;
   const int G = a.group;
@@ -84,18 +114,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   if (ctx < C || ctx > ctx_lim) { bad = true; ctx = max(C, min(ctx, ctx_lim)); }
   const int P = ctx - C;
   const int rows_b = C * G;
-  const int r0 = rb * kPrefillRowsPerBlock + wave * kPrefillRowsPerWave;
-  if (r0 >= rows_b) return;  // no barrier in this kernel: waves leave independently
+  const int wg_r0 = rb * kPrefillRowsPerBlock;
+  if (wg_r0 >= rows_b) return;  // the whole workgroup, before any barrier
 
+  // the workgroup's key range and this wave's
+  const int wg_last = min(rows_b - 1, wg_r0 + kPrefillRowsPerBlock - 1);
+  const int ntiles = (P + wg_last / G + 1 + 31) >> 5;
+  const int r0 = wg_r0 + wave * kPrefillRowsPerWave;
+  const bool wave_live = r0 < rows_b;
+  const int w_last = min(rows_b - 1, r0 + kPrefillRowsPerWave - 1);
+  const int lim_max = wave_live ? P + w_last / G : -1;
+  const int lim_min = P + r0 / G;
   const int row = r0 + col;
   const bool live = row < rows_b;
   const int pos = live ? row / G : 0;
   const int h = g * G + (live ? row - pos * G : 0);
   const int limit = live ? P + pos : -1;
-  const int last_row = min(rows_b - 1, r0 + kPrefillRowsPerWave - 1);
-  const int lim_max = P + last_row / G;
-  const int lim_min = P + r0 / G;
-  const int ntiles = (lim_max + 1 + 31) >> 5;
   const int npages = (ctx + kPage - 1) / kPage;
   const long qrow = ((long)(q0 + pos) * a.hq + h) * D;
 
@@ -125,24 +159,53 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
 
   const int32_t* bt = a.block_tables + (long)b * a.max_blocks;
-  auto page_of = [&](int idx) -> int {
-    int p = bt[idx];
-    if ((unsigned)p >= (unsigned)a.num_pages) { bad = true; p = 0; }
-    return p;
+  auto page_pair = [&](int t, int& pa, int& pb) {
+    pa = bt[2 * t];
+    pb = (2 * t + 1 < npages) ? bt[2 * t + 1] : pa;
+    if ((unsigned)pa >= (unsigned)a.num_pages) { bad = true; pa = 0; }
+    if ((unsigned)pb >= (unsigned)a.num_pages) { bad = true; pb = 0; }
   };
-  // K A-operand row of this lane and the key it carries
-  const int krow = col;
-  const int kpage_sel = krow >> 4;  // 0: first page of the tile, 1: second
-  const int ktok = 8 * ((krow >> 2) & 1) + 4 * ((krow >> 3) & 1) + (krow & 3);
   const long head_elems = (long)kPage * D;
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
 
-  auto load_k = [&](u32x4 (&kf)[NSTEP], int pa, int pb) {
-    const int pg = kpage_sel ? pb : pa;
-    const uint16_t* base = static_cast<const uint16_t*>(a.k_cache) +
-                           ((long)pg * a.hkv + g) * head_elems + (long)ktok * D + 8 * hh;
+  // ---- cooperative tile staging: global -> registers -> LDS
+  u32x4 kst[L::chunks], vst[L::chunks];
+  auto load_regs = [&](int pa, int pb) {
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) kf[s] = *reinterpret_cast<const u32x4*>(base + 16 * s);
+    for (int k = 0; k < L::chunks; ++k) {
+      const int cidx = tid + 256 * k;
+      const int r = cidx / (D / 8), cc = cidx % (D / 8);           // key row, 16-byte chunk
+      const int pg = (r < 16) ? pa : pb;
+      kst[k] = *reinterpret_cast<const u32x4*>(
+          kc + (((long)pg * a.hkv + g) * head_elems + (long)(r & 15) * D) * 2 + cc * 16);
+      const int u = cidx / (2 * D), d = (cidx % (2 * D)) >> 1, half = cidx & 1;
+      const int pv = u ? pb : pa;
+      vst[k] = *reinterpret_cast<const u32x4*>(
+          vc + (((long)pv * a.hkv + g) * head_elems + (long)d * kPage) * 2 + half * 16);
+    }
   };
+  auto store_regs = [&](char* st, int t) {
+    const bool tail = (32 * t + 32 > ctx);
+#pragma unroll
+    for (int k = 0; k < L::chunks; ++k) {
+      const int cidx = tid + 256 * k;
+      const int r = cidx / (D / 8), cc = cidx % (D / 8);
+      *reinterpret_cast<u32x4*>(st + r * L::kRow + cc * 16) = kst[k];
+      const int u = cidx / (2 * D), d = (cidx % (2 * D)) >> 1, half = cidx & 1;
+      u32x4 vv = vst[k];
+      if (tail) {  // keys at or past the context end may hold anything: zero their V
+        const int key0 = 32 * t + 16 * u + 8 * half;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (key0 + e >= ctx) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+      }
+      *reinterpret_cast<u32x4*>(st + L::vOff + d * L::vRow + u * 32 + half * 16) = vv;
+    }
+  };
+
+  // K A-operand row this lane reads
+  const int krow = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -150,61 +213,55 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  u32x4 kcur[NSTEP], knxt[NSTEP];
-  int pa_cur = 0, pb_cur = 0;
-  if (ntiles > 0) {
-    pa_cur = page_of(0);
-    pb_cur = (1 < npages) ? page_of(1) : pa_cur;
-    load_k(kcur, pa_cur, pb_cur);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    // V^T fragments of this tile: A operand rows d = 32*db + col, keys 8*hh..+7
-    u32x4 vf[NDB][2];
+  auto compute = [&](const char* st, int t) {
+    // ---- S^T = K * Q^T; every fragment read is issued before the MFMAs so
+    //      the LDS latency is paid once per tile
+    const char* krp = st + krow * L::kRow + hh * 16;
+    u32x4 kfr[NSTEP];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int pg = u ? pb_cur : pa_cur;
-      const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) +
-                              ((long)pg * a.hkv + g) * head_elems + 8 * hh;
+    for (int k = 0; k < NSTEP; ++k) kfr[k] = *reinterpret_cast<const u32x4*>(krp + 32 * k);
+    const char* vrp = st + L::vOff + col * L::vRow + hh * 16;
+    u32x4 vfr[NDB][2];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        vf[db][u] = *reinterpret_cast<const u32x4*>(vbase + (long)(32 * db + col) * kPage);
+    for (int db = 0; db < NDB; ++db) {
+      vfr[db][0] = *reinterpret_cast<const u32x4*>(vrp + 32 * db * L::vRow);
+      vfr[db][1] = *reinterpret_cast<const u32x4*>(vrp + 32 * db * L::vRow + 32);
     }
-    // next tile's K
-    int pa_n = pa_cur, pb_n = pb_cur;
-    if (t + 1 < ntiles) {
-      pa_n = page_of(2 * t + 2);
-      pb_n = (2 * t + 3 < npages) ? page_of(2 * t + 3) : pa_n;
-      load_k(knxt, pa_n, pb_n);
-    }
-
-    // ---- S^T = K * Q^T
     f32x16 s = {};
 #pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      H8 kf = __builtin_bit_cast(H8, kcur[st]);
-      s = mfma32x32x16(kf, qhi[st], s);
-      if constexpr (QSPLIT) s = mfma32x32x16(kf, qlo[st], s);
+    for (int k = 0; k < NSTEP; ++k) {
+      const H8 kf = __builtin_bit_cast(H8, kfr[k]);
+      s = mfma32x32x16(kf, qhi[k], s);
+      if constexpr (QSPLIT) s = mfma32x32x16(kf, qlo[k], s);
     }
-
     // ---- online softmax for query row `col`; register r holds key
-    //      32t + 16*(r/8) + 8*hh + r%8
-    const int kbase_tok = 32 * t + 8 * hh;
-    const bool need_mask = (32 * t + 31 > lim_min);
+    //      32t + 16*(r/8) + 8*hh + r%8, masked when that exceeds `limit`
     float sc[16];
+    if (32 * t + 31 > lim_min) {
+      const int rel = limit - (32 * t + 8 * hh);   // largest allowed 16*(r/8) + r%8
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[r] * a.scale_log2;
-      if (need_mask && kbase_tok + 16 * (r >> 3) + (r & 7) > limit) x = -INFINITY;
-      sc[r] = x;
+      for (int r = 0; r < 16; ++r) {
+        const float x = s[r] * a.scale_log2;
+        sc[r] = (16 * (r >> 3) + (r & 7) > rel) ? -INFINITY : x;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = s[r] * a.scale_log2;
     }
     float mt = sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    const bool grow = mt > m_run + kLazyRescale;
+    if (__any(grow)) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     H8 p16[2];
     float lsum = 0.f;
 #pragma unroll
@@ -220,54 +277,83 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         lsum += (float)hv;
       }
     }
-    l_part = l_part * alpha + lsum;
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
-
-    // keys at or past the context end may hold anything: zero their V
-    if (32 * t + 32 > ctx) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (32 * t + 16 * u + 8 * hh + e >= ctx) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              vf[db][u][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-        }
-      }
-    }
+    l_part += lsum;
     // ---- O^T += V^T * P^T
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vf[db][0]), p16[0], acc[db]);
-      acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vf[db][1]), p16[1], acc[db]);
+      acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[db][0]), p16[0], acc[db]);
+      acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[db][1]), p16[1], acc[db]);
     }
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st) kcur[st] = knxt[st];
-    pa_cur = pa_n;
-    pb_cur = pb_n;
+  };
+
+  // ---- pipeline: tile t computes from LDS while tile t+1 is in flight
+  int pa_n = 0, pb_n = 0, pa_nn = 0, pb_nn = 0;
+  {
+    int pa0, pb0;
+    page_pair(0, pa0, pb0);
+    load_regs(pa0, pb0);
+    if (ntiles > 1) page_pair(1, pa_n, pb_n);
+    store_regs(lds[0], 0);
   }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) load_regs(pa_n, pb_n);
+    if (t + 2 < ntiles) page_pair(t + 2, pa_nn, pb_nn);
+    if (32 * t <= lim_max) compute(lds[t & 1], t);
+    if (t + 1 < ntiles) store_regs(lds[(t + 1) & 1], t + 1);
+    __syncthreads();
+    pa_n = pa_nn;
+    pb_n = pb_nn;
+  }
+
   const float l_run = l_part + __shfl_xor(l_part, 32);
   if (!live) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float inv = bad ? NAN : (l_run > 0.f ? 1.f / l_run : 0.f);
   const long orow = ((long)(q0 + pos) * a.hq + h) * D;
+  // lane (col + 32*hh), register r of block db holds d = 32*db + 8*(r/4) + 4*hh + r%4:
+  // four consecutive d per group of four registers
+  auto write = [&](auto tag) {
+    using T = decltype(tag);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int d = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
-      float v = acc[db][r] * inv;
-      if (bad) v = NAN;
-      store_from_f32(a.out, orow + d, a.out_dtype, v);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const long o = orow + 32 * db + 8 * r4 + 4 * hh;
+        f32x4 v = {acc[db][4 * r4] * inv, acc[db][4 * r4 + 1] * inv, acc[db][4 * r4 + 2] * inv,
+                   acc[db][4 * r4 + 3] * inv};
+        if constexpr (std::is_same<T, float>::value) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = v;
+        } else {
+          u32x2 pk;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            uint32_t lo, hi;
+            if constexpr (std::is_same<T, __bf16>::value) {
+              lo = f32_to_bf16_bits(v[2 * e]);
+              hi = f32_to_bf16_bits(v[2 * e + 1]);
+            } else {
+              lo = f32_to_f16_bits(v[2 * e]);
+              hi = f32_to_f16_bits(v[2 * e + 1]);
+            }
+            pk[e] = lo | (hi << 16);
+          }
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = pk;
+        }
+      }
     }
-  }
+  };
+  if (a.out_dtype == PKV_F32) write(0.f);
+  else if (a.out_dtype == PKV_BF16) write((__bf16)0.f);
+  else write((_Float16)0.f);
 }
 
 template <int D, int KV>
 static void dispatch_prefill_q(const PrefillArgs& a, pkv_stream_t stream) {
+#ifdef PKV_PREFILL_ROWBLOCK_FASTEST
+  dim3 grid(a.nrowblocks, a.hkv, a.batch);
+#else
   dim3 grid(a.batch, a.hkv, a.nrowblocks);
+#endif
   if (a.q_dtype == KV)
     hipLaunchKernelGGL((prefill_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
   else
