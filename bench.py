@@ -254,7 +254,7 @@ def bench_prefill(g: Gpu, steps: int, warmup: int):
                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": res["tflops_prefill_call"] / BF16_PEAK_TFLOPS,
                        "traffic": profiled_traffic("prefill_C4_counters.txt",
-                                                   source_sha("prefill.hip"))}
+                                                   source_sha("prefill.hip", "pkv_device.h", "pkv_host.h"))}
     return w, res, out
 
 
@@ -325,7 +325,7 @@ def main():
             r["roofline"] = {"bound": "hbm", "achieved": r["decode_call_gbs"], "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": r["decode_call_gbs"] / HBM_PEAK_GBS,
                              "traffic": profiled_traffic(f"decode_{name}_counters.txt",
-                                                         source_sha("decode.hip"))}
+                                                         source_sha("decode.hip", "pkv_device.h", "pkv_host.h"))}
             extras[f"decode_{name}"] = r
     if "C4" in only:
         _, rp, _ = bench_prefill(g, args.steps, args.warmup)
@@ -352,7 +352,7 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(head["decode_call_gbs"] / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("decode_C2_counters.txt",
-                                                     source_sha("decode.hip")),
+                                                     source_sha("decode.hip", "pkv_device.h", "pkv_host.h")),
                          "kernel": "decode_partition_kernel<128,bf16> (the whole paged_attn_decode call: one launch)",
                          "algorithmic_bytes_per_launch": head["effective_kv_bytes"]},
             "detail_C2": head,
