@@ -5,13 +5,13 @@
 //
 // Work split.  A workgroup of 4 waves owns one (sequence b, KV head g, tile
 // of up to 16 query heads, context split).  The context is walked in tiles
-// of 32 tokens (two pages); each wave takes a contiguous quarter of its
-// split.  The page ids of that run are fetched with one vector load (lane i
-// holds the i-th page id) issued together with the context length and the
-// query, since the run's place in the block-table row depends only on the
-// split index; tiles then stream through a ring of register buffers, the
-// next tile's loads in flight while the current one computes.  Each wave
-// keeps its own running max / sum / accumulator; the four waves merge in
+// of 32 tokens (two pages); the tiles a split actually has are divided
+// evenly over the four waves in contiguous runs.  The page ids of a run are
+// fetched with one vector load (lane i holds the i-th page id); tiles then
+// stream through a ring of register buffers, the next tile's loads in
+// flight while the current one computes.  Each wave keeps its own running
+// max / sum / accumulator (the max updated lazily: the accumulator is
+// rescaled only when it grows by more than 2^8); the four waves merge in
 // LDS.  A sequence whose context needs several splits writes normalised
 // partials and a log2-sum-exp per split, merged by decode_reduce_kernel on
 // the same stream (the kernel boundary makes the partials visible across
@@ -60,6 +60,8 @@ struct DecodeArgs {
   int tiles_per_split, nsplits;
   float scale_log2;
 };
+
+constexpr float kDecodeLazyRescale = 8.0f;
 
 // Context length as the kernels use it; flags lengths the block table
 // cannot hold.
@@ -142,7 +144,7 @@ __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs
 #endif
 
 template <int D, int KV>
-__global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves, PKV_DECODE_MIN_WAVES) void decode_partition_kernel(DecodeArgs a) {
   constexpr bool kF32 = (KV == PKV_F32);
   constexpr bool kI8 = (KV == PKV_I8);
   constexpr bool kBF16 = (KV == PKV_BF16);
@@ -162,14 +164,10 @@ __global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_ke
   const int h0 = g * a.group + ht * 16;
   const int nh = min(16, a.group - ht * 16);
 
-  // ---- first round trip: context length, this wave's page ids, the query
+  // ---- first round trip: context length and the query; the page ids
+  //      follow as soon as the context length says how the split's tiles
+  //      divide over the waves
   const int raw_ctx = a.context_lens[b];
-  const int tpw = a.tiles_per_split / kDecodeWaves;
-  const int wt0 = split * a.tiles_per_split + wave * tpw;   // first tile of the wave
-  const int wp0 = 2 * wt0;                                  // its first page
-  int pid = 0;
-  if (lane < 2 * tpw && wp0 + lane < a.max_blocks)
-    pid = a.block_tables[(long)b * a.max_blocks + wp0 + lane];
 
   float qf[kF32 ? NSTEP : 1];
   H8 qhi[kF32 ? 1 : NSTEP], qlo[kF32 ? 1 : NSTEP];
@@ -208,9 +206,19 @@ __global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_ke
   const int nsplit_b = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
   if (split >= (nsplit_b > 0 ? nsplit_b : 1)) return;
   const int npages = (ctx + kPage - 1) / kPage;
-  const int ntw = max(0, min(ntiles - wt0, tpw));
+  // the split's tiles, divided evenly over the waves in contiguous runs
+  const int st0 = split * a.tiles_per_split;
+  const int stn = max(0, min(ntiles - st0, a.tiles_per_split));
+  const int per = (stn + kDecodeWaves - 1) / kDecodeWaves;   // <= 32
+  const int wt0 = st0 + wave * per;                          // first tile of the wave
+  const int ntw = max(0, min(st0 + stn - wt0, per));
+  const int wp0 = 2 * wt0;                                   // its first page
   const int npw = max(0, min(npages - wp0, 2 * ntw));
-  if (lane < npw && (unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
+  int pid = 0;
+  if (lane < npw) {
+    pid = a.block_tables[(long)b * a.max_blocks + wp0 + lane];
+    if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
+  }
 
   f32x4 acc[NBLK];
 #pragma unroll
@@ -259,24 +267,38 @@ __global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_ke
       s2[u] = sacc;
     }
 
-    // ---- scores of head c for tile tokens 8j + e, e = 4u + i
+    // ---- scores of head c for tile tokens 8j + e, e = 4u + i; only the
+    //      tile holding the context end needs masking
     const int t = wt0 + li;
     const int tok0 = 32 * t + 8 * j;
+    const bool partial = (32 * t + 32 > ctx);
     float sc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = s2[e >> 2][e & 3] * a.scale_log2;
       if constexpr (kI8) x *= cur.ks[e >> 2][e & 3];
-      sc[e] = (tok0 + e < ctx) ? x : -INFINITY;
+      sc[e] = x;
+    }
+    if (partial) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (tok0 + e >= ctx) sc[e] = -INFINITY;
     }
     float mt = sc[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
     mt = wave_max_xor_16_32(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    // lazy running max: the accumulator is rescaled only when the max grows
+    // by more than 2^8; the stale max cancels in the final normalisation
+    if (__any(mt > m_run + kDecodeLazyRescale)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < NBLK; ++i) acc[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float p[8];
     float lsum = 0.f;
 #pragma unroll
@@ -284,11 +306,8 @@ __global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_ke
       p[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
       lsum += p[e];
     }
-    l_part = l_part * alpha + lsum;
-#pragma unroll
-    for (int i = 0; i < NBLK; ++i) acc[i] *= alpha;
+    l_part += lsum;
 
-    const bool partial = (32 * t + 32 > ctx);
     // ---- O^T += V^T * P^T
     if constexpr (kF32) {
 #pragma unroll
@@ -307,6 +326,13 @@ __global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_ke
         float x = p[e];
         if constexpr (kI8) x = (tok0 + e < ctx) ? x * cur.vs[e >> 2][e & 3] : 0.f;
         pv[e] = x;
+      }
+      // V of tokens at or past the context end may hold anything: zero them
+      u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+      if (partial) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (tok0 + e >= ctx) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
       }
       H8 phi, plo;
       if constexpr (kBF16) {
@@ -327,12 +353,7 @@ __global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_ke
           vf = tmp;
         } else {
           u32x4 wv = cur.v[blk][0];
-          if (partial) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (tok0 + e >= ctx) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-            }
-          }
+          if (partial) wv &= vmask;
           vf = __builtin_bit_cast(H8, wv);
         }
         acc[blk] = mfma16x16x32(vf, phi, acc[blk]);
@@ -378,7 +399,7 @@ __global__ __launch_bounds__(256, PKV_DECODE_MIN_WAVES) void decode_partition_ke
   __syncthreads();
   const bool any_bad = s_bad != 0;
   const bool direct = nsplit_b <= 1;
-  for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < nh * D; idx += 64 * kDecodeWaves) {
     const int hc = idx / D, d = idx - hc * D;
     float M = s_m[0][hc];
 #pragma unroll

@@ -30,7 +30,10 @@ struct DecodePlan {
 };
 
 constexpr int kDecodeTileTokens = 32;
-constexpr int kDecodeWaves = 4;
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PKV_DECODE_WAVES;
 // A wave's page ids are held one per lane, so a wave takes at most 32 tiles.
 constexpr int kDecodeMaxTilesPerSplit = 32 * kDecodeWaves;
 // The merge kernel holds one split per lane.
