@@ -115,16 +115,30 @@ __device__ __forceinline__ void i8x8_to_f16x8(u32x2 w, f16x8& out) {
   }
 }
 
-__device__ __forceinline__ float wave_max_xor_16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Cross-lane exchanges with the gfx950 lane-swap instructions (VALU, no LDS
+// round trip).  v_permlane32_swap exchanges the upper 32 lanes of one
+// operand with the lower 32 of the other; given x in both, the two results
+// hold, in every lane l, x[l] and x[l ^ 32] (which result holds which does not
+// matter to a max or a sum).  v_permlane16_swap does the same for lanes
+// l and l ^ 16.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float wave_sum_xor_16_32(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
+__device__ __forceinline__ float wave_max_xor_16_32(float x) { return max_xor32(max_xor16(x)); }
+__device__ __forceinline__ float wave_sum_xor_16_32(float x) { return sum_xor32(sum_xor16(x)); }
 
 }  // namespace pkv

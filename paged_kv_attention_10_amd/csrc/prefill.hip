@@ -31,7 +31,8 @@
 //
 // Precision: q and K/V in the cache's 16-bit type (an fp32 or other-typed
 // q is split into head + remainder and multiplied twice), P rounded to the
-// 16-bit type (the normaliser sums the rounded values), fp32 accumulation.
+// 16-bit type for PV (the normaliser sums the fp32 values), fp32
+// accumulation.
 #include <math.h>
 
 #include <type_traits>
@@ -235,23 +236,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       if constexpr (QSPLIT) s = mfma32x32x16(kf, qlo[k], s);
     }
     // ---- online softmax for query row `col`; register r holds key
-    //      32t + 16*(r/8) + 8*hh + r%8, masked when that exceeds `limit`
+    //      32t + 16*(r/8) + 8*hh + r%8, masked when that exceeds `limit`.
+    //      Raw scores are masked and maximised; the log2e-prescaled scale
+    //      (positive) is applied inside the exponent: p = 2^(s*c - m).
     float sc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = s[r];
     if (32 * t + 31 > lim_min) {
       const int rel = limit - (32 * t + 8 * hh);   // largest allowed 16*(r/8) + r%8
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = s[r] * a.scale_log2;
-        sc[r] = (16 * (r >> 3) + (r & 7) > rel) ? -INFINITY : x;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = s[r] * a.scale_log2;
+      for (int r = 0; r < 16; ++r)
+        if (16 * (r >> 3) + (r & 7) > rel) sc[r] = -INFINITY;
     }
     float mt = sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = max_xor32(mt) * a.scale_log2;
     const bool grow = mt > m_run + kLazyRescale;
     if (__any(grow)) {
       const float m_new = grow ? mt : m_run;
@@ -266,16 +266,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = __builtin_amdgcn_exp2f(sc[r] - m_use);
-      if constexpr (kBF16) {
-        __bf16 hv = (__bf16)p;
-        p16[r >> 3][r & 7] = hv;
-        lsum += (float)hv;
-      } else {
-        _Float16 hv = (_Float16)p;
-        p16[r >> 3][r & 7] = hv;
-        lsum += (float)hv;
-      }
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, -m_use));
+      lsum += p;
+      if constexpr (kBF16) p16[r >> 3][r & 7] = (__bf16)p;
+      else p16[r >> 3][r & 7] = (_Float16)p;
     }
     l_part += lsum;
     // ---- O^T += V^T * P^T
@@ -306,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     pb_n = pb_nn;
   }
 
-  const float l_run = l_part + __shfl_xor(l_part, 32);
+  const float l_run = sum_xor32(l_part);
   if (!live) return;
   const float inv = bad ? NAN : (l_run > 0.f ? 1.f / l_run : 0.f);
   const long orow = ((long)(q0 + pos) * a.hq + h) * D;
