@@ -5,7 +5,8 @@ Headline workload: paged decode with a bf16 KV cache at the Qwen2.5-1.5B
 attention shape (batch 64, 12 query / 2 KV heads, head_dim 128, 16-token
 pages, context lengths uniform in [512, 4096], pages scattered over a
 20k-page pool).  One step = append of the step's 64 new tokens + the decode
-call (one kernel: partitions + in-kernel log-sum-exp merge).  Before every
+call (the split-context partition kernel, then the log-sum-exp reduce
+kernel on the same stream when a context is split).  Before every
 timed step a 1 GiB read evicts L2 and the 256 MB MALL, so every step reads
 its KV from HBM; each step is timed with HIP events on the stream the
 library launches on (the flush is outside the events).
@@ -344,7 +345,7 @@ def main():
             "config": {"workload": DESC["C2"], "batch": 64, "num_q_heads": 12, "num_kv_heads": 2,
                        "head_dim": 128, "page_size": 16, "kv_dtype": "bf16",
                        "context_tokens": int(w2.context_lens.sum()),
-                       "step": "append of 64 new tokens + decode (one kernel: partitions + in-kernel LSE merge)",
+                       "step": "append of 64 new tokens + decode (partition kernel, then LSE reduce kernel)",
                        "timing": "HIP events per step on the library's stream; 1 GiB read-only flush before each step, outside the events"},
             "hbm_frac": round(head["hbm_frac_step"], 4),
             "seq_tokens_per_s": round(head["seq_tokens_per_s"], 1),
@@ -353,7 +354,7 @@ def main():
                          "frac": round(head["decode_call_gbs"] / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("decode_C2_counters.txt",
                                                      source_sha("decode.hip", "pkv_device.h", "pkv_host.h")),
-                         "kernel": "decode_partition_kernel<128,bf16> (the whole paged_attn_decode call: one launch)",
+                         "kernel": "paged_attn_decode call: decode_partition_kernel<128,bf16> + decode_reduce_kernel<128>, events around both",
                          "algorithmic_bytes_per_launch": head["effective_kv_bytes"]},
             "detail_C2": head,
         })

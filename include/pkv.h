@@ -172,6 +172,8 @@ size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_
  *                  cu_q_lens[batch] == num_tokens, each C_b <= max_q_len.
  *   context_lens   [batch] int32 = P_b + C_b, each <= max_context_len.
  *   out            [num_tokens][num_q_heads][head_dim], dtype out_dtype.
+ *                  q and out may be NULL when num_tokens == 0, which is a
+ *                  no-op returning PKV_OK once the other arguments check.
  *   workspace      at least paged_attn_prefill_workspace_bytes(...) bytes.
  *   other arguments as for paged_attn_decode.
  *

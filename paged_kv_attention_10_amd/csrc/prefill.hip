@@ -383,7 +383,8 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
                                         void* out, int out_dtype, void* workspace,
                                         size_t workspace_bytes, pkv_stream_t stream) {
   (void)workspace; (void)workspace_bytes;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens || !out)
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens ||
+      ((!q || !out) && num_tokens > 0))
     return PKV_ERR_INVALID_ARG;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
       num_pages <= 0 || max_blocks_per_seq <= 0 || num_tokens < 0 || max_q_len < 0 ||
