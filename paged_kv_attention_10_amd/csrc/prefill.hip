@@ -7,22 +7,29 @@
 // Rows.  The query rows of one (sequence, KV head) are the chunk positions
 // times the G query heads that share the KV head, flattened head-fastest:
 // row r -> position r / G, head g*G + r % G.  A workgroup of 4 waves owns 128
-// consecutive rows, a wave 32.  The workgroup walks the key tiles its rows
-// need (32 keys = two pages per tile); each tile's K and V^T are loaded once,
-// cooperatively, into LDS (double-buffered, rows padded so the fragment
-// reads are free of bank conflicts) and read by all four waves, so the G
-// heads of a position and the 32-row blocks of the chunk share every load.
-// Page ids are fetched two tiles ahead; tiles past a wave's causal limit
-// skip its math.
+// consecutive rows, a wave 32.  The workgroup walks the key range its rows
+// need in tiles of 64 keys (4 pages).  Wave w copies page w of the next tile
+// (its K block and its V^T block) straight from HBM into LDS with
+// global_load_lds (no register staging) while all four waves compute on
+// the current tile, so the G heads of a position and the 32-row blocks of
+// the chunk share every load; one barrier per 64 keys.  Page ids come from a
+// 64-page window held one per lane and read with readlane.
 //
-// MFMA mapping (32x32x16, wave64).  S^T = K * Q^T: A = K (row = key),
-// B = Q^T (column = query row).  The A-operand row rho reads key
-// 16*(rho/16) + 8*((rho/4)&1) + 4*((rho/8)&1) + rho%4, which makes lane
-// (c + 32*h) hold, for query row c, the scores of keys 8h..8h+7 of the first
-// page (registers 0-7) and of the second page (registers 8-15): the
-// B-operand layout of O^T = V^T * P^T with no data movement.  The V page is
-// stored token-innermost, so each V^T A-operand read is a contiguous 8-key
-// run.  The causal mask is applied only to tiles that cross a row's limit.
+// LDS (per stage, double-buffered): K as 64 key rows of D elements whose
+// 16-byte chunks are XOR-swizzled by the row's position in its page, and
+// V^T as four page blocks [d][16 keys] exactly as they lie in HBM.  Both
+// fragment reads below are free of bank conflicts on gfx950 (64 banks; a
+// 16-byte read from 64 lanes costs the largest number of lanes that share a
+// 16-byte slot of the 256-byte bank space, at best 4).
+//
+// MFMA mapping (32x32x16, wave64), per 32-key half of a tile: S^T = K * Q^T
+// with A = K (row = key), B = Q^T (column = query row).  The A-operand row
+// rho reads key 16*(rho/16) + 8*((rho/4)&1) + 4*((rho/8)&1) + rho%4, which
+// makes lane (c + 32*h) hold, for query row c, the scores of keys 8h..8h+7
+// of the half's first page (registers 0-7) and of its second page
+// (registers 8-15): the B-operand layout of O^T = V^T * P^T with no data
+// movement.  Each V^T A-operand read is a contiguous 8-key run of one d row.
+// The causal mask runs only on halves that cross a row's limit.
 //
 // Softmax.  exp2 of log2e-prescaled scores with a lazily updated running
 // max: the accumulator is rescaled only when a row's max grows by more than
@@ -51,9 +58,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// 16 bytes per lane from global memory into LDS at l + 16 * lane (l must be
+// the same in every lane of the wave).
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRowsPerBlock = kPrefillRowsPerWave * kPrefillWaves;
+constexpr int kPrefillTileKeys = 64;  // 4 pages, one per wave
 
 struct PrefillArgs {
   const void* q;
@@ -69,16 +84,23 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-// LDS tile layout (per stage): K as 32 key rows of D elements padded by 16
-// bytes; V^T as D rows of 32 keys padded by 16 bytes.
 template <int D>
 struct PrefillLds {
-  static constexpr int kRow = D * 2 + 16;
-  static constexpr int vRow = 32 * 2 + 16;
-  static constexpr int vOff = 32 * kRow;
-  static constexpr int stage = vOff + D * vRow;
-  static constexpr int chunks = D / 64;   // 16-byte chunks per thread, each of K and V
+  static constexpr int kRow = 2 * D;                 // bytes of one K row
+  static constexpr int kPageBytes = kPage * kRow;    // one page of K (= one page of V^T)
+  static constexpr int vOff = 4 * kPageBytes;        // V^T blocks after the 64 K rows
+  static constexpr int stage = 8 * kPageBytes;
+  static constexpr int dmaPerPage = kPageBytes / 1024;
+  static constexpr int chunksPerRow = D / 8;
 };
+
+// 16-byte-chunk swizzle of K row rr (its offset in the page): chunk c of the
+// row is stored in slot c ^ swz(rr).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int rr) {
+  if constexpr (D == 128) return (rr ^ ((rr & 8) >> 1)) & 15;
+  else return (rr ^ (rr >> 3)) & 7;
+}
 
 constexpr float kLazyRescale = 8.0f;
 
@@ -89,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using L = PrefillLds<D>;
   constexpr int NSTEP = D / 16;  // QK k-steps of 16
   constexpr int NDB = D / 32;    // 32-row blocks of d for PV
-  __shared__ __attribute__((aligned(16))) char lds[2][L::stage];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * L::stage];
 
 #ifdef PKV_PREFILL_ROWBLOCK_FASTEST
   const int rb = a.nrowblocks - 1 - (int)blockIdx.x;
@@ -100,7 +122,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #endif
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int hh = lane >> 5;
@@ -120,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   // the workgroup's key range and this wave's
   const int wg_last = min(rows_b - 1, wg_r0 + kPrefillRowsPerBlock - 1);
-  const int ntiles = (P + wg_last / G + 1 + 31) >> 5;
+  const int ntiles = (P + wg_last / G + kPrefillTileKeys) / kPrefillTileKeys;
   const int r0 = wg_r0 + wave * kPrefillRowsPerWave;
   const bool wave_live = r0 < rows_b;
   const int w_last = min(rows_b - 1, r0 + kPrefillRowsPerWave - 1);
@@ -159,54 +181,55 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
+  // ---- page ids: a window of 64 consecutive entries of the block-table row,
+  //      one per lane, and the next window loaded ahead
   const int32_t* bt = a.block_tables + (long)b * a.max_blocks;
-  auto page_pair = [&](int t, int& pa, int& pb) {
-    pa = bt[2 * t];
-    pb = (2 * t + 1 < npages) ? bt[2 * t + 1] : pa;
-    if ((unsigned)pa >= (unsigned)a.num_pages) { bad = true; pa = 0; }
-    if ((unsigned)pb >= (unsigned)a.num_pages) { bad = true; pb = 0; }
+  auto load_window = [&](int win) {
+    const int i = 64 * win + lane;
+    return i < npages ? bt[i] : 0;
   };
-  const long head_elems = (long)kPage * D;
+  int pid_cur = load_window(0);
+  int pid_next = ntiles > 16 ? load_window(1) : 0;
+
+  // ---- tile copy: wave w moves page 4t + w of the tile (K rows swizzled,
+  //      V^T block as is) into stage `stg`; pages past the context are not
+  //      read (their keys are masked and their V is zeroed in registers)
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
-
-  // ---- cooperative tile staging: global -> registers -> LDS
-  u32x4 kst[L::chunks], vst[L::chunks];
-  auto load_regs = [&](int pa, int pb) {
+  int koff[L::dmaPerPage];
 #pragma unroll
-    for (int k = 0; k < L::chunks; ++k) {
-      const int cidx = tid + 256 * k;
-      const int r = cidx / (D / 8), cc = cidx % (D / 8);           // key row, 16-byte chunk
-      const int pg = (r < 16) ? pa : pb;
-      kst[k] = *reinterpret_cast<const u32x4*>(
-          kc + (((long)pg * a.hkv + g) * head_elems + (long)(r & 15) * D) * 2 + cc * 16);
-      const int u = cidx / (2 * D), d = (cidx % (2 * D)) >> 1, half = cidx & 1;
-      const int pv = u ? pb : pa;
-      vst[k] = *reinterpret_cast<const u32x4*>(
-          vc + (((long)pv * a.hkv + g) * head_elems + (long)d * kPage) * 2 + half * 16);
+  for (int j = 0; j < L::dmaPerPage; ++j) {
+    const int byte = 1024 * j + 16 * lane;          // position inside the page's K block
+    const int rr = byte / L::kRow, slot = (byte % L::kRow) / 16;
+    koff[j] = rr * L::kRow + ((slot ^ k_swizzle<D>(rr)) * 16);
+  }
+  auto issue_tile = [&](int t, int stg) {
+    if ((t & 15) == 0 && t > 0) {
+      pid_cur = pid_next;
+      pid_next = load_window((t >> 4) + 1);
     }
-  };
-  auto store_regs = [&](char* st, int t) {
-    const bool tail = (32 * t + 32 > ctx);
+    const int pi = 4 * t + wave;
+    if (pi < npages) {
+      int pid = __builtin_amdgcn_readlane(pid_cur, pi & 63);
+      if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
+      const long blk = ((long)pid * a.hkv + g) * L::kPageBytes;
+      char* lk = lds + stg * L::stage + wave * L::kPageBytes;
+      char* lv = lds + stg * L::stage + L::vOff + wave * L::kPageBytes;
 #pragma unroll
-    for (int k = 0; k < L::chunks; ++k) {
-      const int cidx = tid + 256 * k;
-      const int r = cidx / (D / 8), cc = cidx % (D / 8);
-      *reinterpret_cast<u32x4*>(st + r * L::kRow + cc * 16) = kst[k];
-      const int u = cidx / (2 * D), d = (cidx % (2 * D)) >> 1, half = cidx & 1;
-      u32x4 vv = vst[k];
-      if (tail) {  // keys at or past the context end may hold anything: zero their V
-        const int key0 = 32 * t + 16 * u + 8 * half;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (key0 + e >= ctx) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+      for (int j = 0; j < L::dmaPerPage; ++j) {
+        dma16(kc + blk + koff[j], lk + 1024 * j);
+        dma16(vc + blk + 1024 * j + 16 * lane, lv + 1024 * j);
       }
-      *reinterpret_cast<u32x4*>(st + L::vOff + d * L::vRow + u * 32 + half * 16) = vv;
     }
   };
 
-  // K A-operand row this lane reads
+  // per-lane LDS offsets of the fragment reads
   const int krow = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
+  int kaddr[NSTEP];
+#pragma unroll
+  for (int k = 0; k < NSTEP; ++k)
+    kaddr[k] = krow * L::kRow + (((2 * k + hh) ^ k_swizzle<D>(krow & 15)) * 16);
+  const int vaddr = L::vOff + col * 32 + hh * 16;
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -214,20 +237,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  auto compute = [&](const char* st, int t) {
-    // ---- S^T = K * Q^T; every fragment read is issued before the MFMAs so
-    //      the LDS latency is paid once per tile
-    const char* krp = st + krow * L::kRow + hh * 16;
+  // one 32-key half (keys kb .. kb+31, pages 2*half and 2*half+1 of the tile)
+  auto compute_half = [&](const char* st, int half, int kb) {
+    // ---- S^T = K * Q^T; every fragment read is issued before the MFMAs
     u32x4 kfr[NSTEP];
 #pragma unroll
-    for (int k = 0; k < NSTEP; ++k) kfr[k] = *reinterpret_cast<const u32x4*>(krp + 32 * k);
-    const char* vrp = st + L::vOff + col * L::vRow + hh * 16;
+    for (int k = 0; k < NSTEP; ++k)
+      kfr[k] = *reinterpret_cast<const u32x4*>(st + half * 32 * L::kRow + kaddr[k]);
     u32x4 vfr[NDB][2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      vfr[db][0] = *reinterpret_cast<const u32x4*>(vrp + 32 * db * L::vRow);
-      vfr[db][1] = *reinterpret_cast<const u32x4*>(vrp + 32 * db * L::vRow + 32);
-    }
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        vfr[db][j] = *reinterpret_cast<const u32x4*>(st + vaddr + (2 * half + j) * L::kPageBytes +
+                                                     db * 32 * 32);
     f32x16 s = {};
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
@@ -235,15 +258,29 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       s = mfma32x32x16(kf, qhi[k], s);
       if constexpr (QSPLIT) s = mfma32x32x16(kf, qlo[k], s);
     }
+    // keys at or past the context end may hold anything: zero their V
+    if (kb + 32 > ctx) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int key0 = kb + 16 * j + 8 * hh;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (key0 + e >= ctx) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              vfr[db][j][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+      }
+    }
     // ---- online softmax for query row `col`; register r holds key
-    //      32t + 16*(r/8) + 8*hh + r%8, masked when that exceeds `limit`.
+    //      kb + 16*(r/8) + 8*hh + r%8, masked when that exceeds `limit`.
     //      Raw scores are masked and maximised; the log2e-prescaled scale
     //      (positive) is applied inside the exponent: p = 2^(s*c - m).
     float sc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = s[r];
-    if (32 * t + 31 > lim_min) {
-      const int rel = limit - (32 * t + 8 * hh);   // largest allowed 16*(r/8) + r%8
+    if (kb + 31 > lim_min) {
+      const int rel = limit - (kb + 8 * hh);   // largest allowed 16*(r/8) + r%8
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (16 * (r >> 3) + (r & 7) > rel) sc[r] = -INFINITY;
@@ -280,25 +317,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- pipeline: tile t computes from LDS while tile t+1 is in flight
-  int pa_n = 0, pb_n = 0, pa_nn = 0, pb_nn = 0;
-  {
-    int pa0, pb0;
-    page_pair(0, pa0, pb0);
-    load_regs(pa0, pb0);
-    if (ntiles > 1) page_pair(1, pa_n, pb_n);
-    store_regs(lds[0], 0);
-  }
-  __syncthreads();
+  // ---- pipeline: tile t computes from LDS while tile t+1 is copied in
+  issue_tile(0, 0);
+  __syncthreads();  // waits for this wave's copies, then for every wave's
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_regs(pa_n, pb_n);
-    if (t + 2 < ntiles) page_pair(t + 2, pa_nn, pb_nn);
-    if (32 * t <= lim_max) compute(lds[t & 1], t);
-    if (t + 1 < ntiles) store_regs(lds[(t + 1) & 1], t + 1);
+    if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
+    const char* st = lds + (t & 1) * L::stage;
+    const int kb = t * kPrefillTileKeys;
+    // every wave computes every half: a half past all of a wave's rows is
+    // fully masked (p = 0), and branching around it would make the compiler
+    // copy the accumulators at each join
+    compute_half(st, 0, kb);
+    compute_half(st, 1, kb + 32);
     __syncthreads();
-    pa_n = pa_nn;
-    pb_n = pb_nn;
   }
+  bad = __syncthreads_or(bad);
 
   const float l_run = sum_xor32(l_part);
   if (!live) return;
