@@ -20,9 +20,9 @@ inline int launch_status() { return hipGetLastError() == hipSuccess ? PKV_OK : P
 
 // How a decode call is cut into work: contexts are processed in tiles of 32
 // tokens (two pages); a workgroup of 4 waves owns `tiles_per_split` tiles of
-// one (sequence, KV head, head tile), each wave a contiguous quarter of them;
-// `nsplits` workgroups cover the longest context.  A pure function of the
-// shapes, so the workspace query and the launch agree.
+// one (sequence, KV head, head tile), its waves an equal share of the tiles
+// the split actually holds; `nsplits` workgroups cover the longest context.
+// A pure function of the shapes, so the workspace query and the launch agree.
 struct DecodePlan {
   int head_tiles;
   int tiles_per_split;

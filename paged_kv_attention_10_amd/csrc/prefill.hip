@@ -144,10 +144,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int wg_last = min(rows_b - 1, wg_r0 + kPrefillRowsPerBlock - 1);
   const int ntiles = (P + wg_last / G + kPrefillTileKeys) / kPrefillTileKeys;
   const int r0 = wg_r0 + wave * kPrefillRowsPerWave;
-  const bool wave_live = r0 < rows_b;
-  const int w_last = min(rows_b - 1, r0 + kPrefillRowsPerWave - 1);
-  const int lim_max = wave_live ? P + w_last / G : -1;
-  const int lim_min = P + r0 / G;
+  const int lim_min = P + r0 / G;      // smallest causal limit among the wave's rows
   const int row = r0 + col;
   const bool live = row < rows_b;
   const int pos = live ? row / G : 0;
@@ -237,57 +234,72 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  // one 32-key half (keys kb .. kb+31, pages 2*half and 2*half+1 of the tile)
-  auto compute_half = [&](const char* st, int half, int kb) {
-    // ---- S^T = K * Q^T; every fragment read is issued before the MFMAs
-    u32x4 kfr[NSTEP];
+  // one 64-key tile (keys kb .. kb+63; half hf = pages 2hf and 2hf+1)
+  auto compute_tile = [&](const char* st, int kb) {
+    // ---- S^T = K * Q^T for both halves: all K fragment reads first (one
+    //      LDS latency), then two independent MFMA chains
+    u32x4 kfr[2][NSTEP];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int k = 0; k < NSTEP; ++k)
+        kfr[hf][k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kaddr[k]);
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k)
-      kfr[k] = *reinterpret_cast<const u32x4*>(st + half * 32 * L::kRow + kaddr[k]);
-    u32x4 vfr[NDB][2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int hf = 0; hf < 2; ++hf) {
+        const H8 kf = __builtin_bit_cast(H8, kfr[hf][k]);
+        s[hf] = mfma32x32x16(kf, qhi[k], s[hf]);
+        if constexpr (QSPLIT) s[hf] = mfma32x32x16(kf, qlo[k], s[hf]);
+      }
+    // keep the K reads ahead of the MFMAs (the default schedule pairs them
+    // and waits for LDS between every two MFMAs)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NSTEP, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, (QSPLIT ? 4 : 2) * NSTEP, 0);
+    // ---- V^T fragments (their LDS latency hides behind the softmax)
+    u32x4 vfr[2][NDB][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        vfr[db][j] = *reinterpret_cast<const u32x4*>(st + vaddr + (2 * half + j) * L::kPageBytes +
-                                                     db * 32 * 32);
-    f32x16 s = {};
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-      const H8 kf = __builtin_bit_cast(H8, kfr[k]);
-      s = mfma32x32x16(kf, qhi[k], s);
-      if constexpr (QSPLIT) s = mfma32x32x16(kf, qlo[k], s);
-    }
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          vfr[hf][db][j] = *reinterpret_cast<const u32x4*>(
+              st + vaddr + (2 * hf + j) * L::kPageBytes + db * 32 * 32);
     // keys at or past the context end may hold anything: zero their V
-    if (kb + 32 > ctx) {
+    if (kb + 64 > ctx) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int key0 = kb + 16 * j + 8 * hh;
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (key0 + e >= ctx) {
+        for (int j = 0; j < 2; ++j) {
+          const int key0 = kb + 32 * hf + 16 * j + 8 * hh;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              vfr[db][j][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t m = (key0 + e >= ctx) ? ((e & 1) ? 0x0000ffffu : 0xffff0000u) : 0xffffffffu;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) vfr[hf][db][j][e >> 1] &= m;
           }
+        }
+    }
+    // ---- online softmax for query row `col`; register r of half hf holds
+    //      key kb + 32*hf + 16*(r/8) + 8*hh + r%8, masked when that exceeds
+    //      `limit`.  Raw scores are masked and maximised; the log2e-prescaled
+    //      scale (positive) is applied inside the exponent: p = 2^(s*c - m).
+    if (kb + 63 > lim_min) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int rel = limit - (kb + 32 * hf + 8 * hh);   // largest allowed 16*(r/8) + r%8
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + (r & 7) > rel) s[hf][r] = -INFINITY;
       }
     }
-    // ---- online softmax for query row `col`; register r holds key
-    //      kb + 16*(r/8) + 8*hh + r%8, masked when that exceeds `limit`.
-    //      Raw scores are masked and maximised; the log2e-prescaled scale
-    //      (positive) is applied inside the exponent: p = 2^(s*c - m).
-    float sc[16];
+    float mt = s[0][0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = s[r];
-    if (kb + 31 > lim_min) {
-      const int rel = limit - (kb + 8 * hh);   // largest allowed 16*(r/8) + r%8
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (16 * (r >> 3) + (r & 7) > rel) sc[r] = -INFINITY;
-    }
-    float mt = sc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
     mt = max_xor32(mt) * a.scale_log2;
     const bool grow = mt > m_run + kLazyRescale;
     if (__any(grow)) {
@@ -299,22 +311,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    H8 p16[2];
     float lsum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, -m_use));
-      lsum += p;
-      if constexpr (kBF16) p16[r >> 3][r & 7] = (__bf16)p;
-      else p16[r >> 3][r & 7] = (_Float16)p;
+    for (int hf = 0; hf < 2; ++hf) {
+      H8 p16[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][r], a.scale_log2, -m_use));
+        lsum += p;
+        if constexpr (kBF16) p16[r >> 3][r & 7] = (__bf16)p;
+        else p16[r >> 3][r & 7] = (_Float16)p;
+      }
+      // ---- O^T += V^T * P^T
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[hf][db][j]), p16[j], acc[db]);
     }
     l_part += lsum;
-    // ---- O^T += V^T * P^T
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[db][0]), p16[0], acc[db]);
-      acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[db][1]), p16[1], acc[db]);
-    }
   };
 
   // ---- pipeline: tile t computes from LDS while tile t+1 is copied in
@@ -324,11 +339,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
     const char* st = lds + (t & 1) * L::stage;
     const int kb = t * kPrefillTileKeys;
-    // every wave computes every half: a half past all of a wave's rows is
+    // every wave computes every tile: a tile past all of a wave's rows is
     // fully masked (p = 0), and branching around it would make the compiler
     // copy the accumulators at each join
-    compute_half(st, 0, kb);
-    compute_half(st, 1, kb + 32);
+    compute_tile(st, kb);
     __syncthreads();
   }
   bad = __syncthreads_or(bad);
