@@ -164,10 +164,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves, PKV_DECODE_MIN_WAVES) void decod
   const int h0 = g * a.group + ht * 16;
   const int nh = min(16, a.group - ht * 16);
 
-  // ---- first round trip: context length and the query; the page ids
-  //      follow as soon as the context length says how the split's tiles
-  //      divide over the waves
+  // ---- one round trip for the context length, the query and the page ids
+  //      of the whole split (loaded before the context length says which of
+  //      them the split uses and how its tiles divide over the waves; entries
+  //      past the context are never used)
   const int raw_ctx = a.context_lens[b];
+  __shared__ int s_pid[2 * kDecodeMaxTilesPerSplit];
+  {
+    const int sp0 = 2 * split * a.tiles_per_split;          // the split's first page
+    const int i = threadIdx.x;
+    if (i < 2 * a.tiles_per_split && sp0 + i < a.max_blocks)
+      s_pid[i] = a.block_tables[(long)b * a.max_blocks + sp0 + i];
+  }
 
   float qf[kF32 ? NSTEP : 1];
   H8 qhi[kF32 ? 1 : NSTEP], qlo[kF32 ? 1 : NSTEP];
@@ -214,9 +222,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves, PKV_DECODE_MIN_WAVES) void decod
   const int ntw = max(0, min(st0 + stn - wt0, per));
   const int wp0 = 2 * wt0;                                   // its first page
   const int npw = max(0, min(npages - wp0, 2 * ntw));
+  __syncthreads();   // the split's page ids are in LDS
   int pid = 0;
   if (lane < npw) {
-    pid = a.block_tables[(long)b * a.max_blocks + wp0 + lane];
+    pid = s_pid[wp0 - 2 * st0 + lane];
     if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
   }
 
