@@ -196,6 +196,44 @@ int paged_attn_prefill_chunk(const void* q, int q_dtype,
 size_t paged_attn_prefill_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
                                           int head_dim, int max_q_len, int max_context_len);
 
+/*
+ * paged_attn_mixed - prefill chunks and decode tokens of one batch in one call.
+ *
+ * Chunked prefill/decode scheduling over the paged cache (Tiny-LLM "Project
+ * Status", supported features: chunked prefill/decode scheduling; TinyLoop
+ * "Current Status", table "Model architecture support", row "Chunked
+ * prefill").  Arguments, layouts and results are exactly those of
+ * paged_attn_prefill_chunk (a decode token is a chunk of one: its query row
+ * cu_q_lens[b] attends to [0, context_lens[b])); the difference is how the
+ * work is cut: sequences whose chunk is a single token have their context
+ * split across several workgroups as in paged_attn_decode, the others run
+ * the MFMA prefill row blocks, all in one launch (plus the split merge).
+ *
+ *   workspace      at least paged_attn_mixed_workspace_bytes(...) bytes (the
+ *                  decode split partials; may be NULL when that is 0); its
+ *                  contents on entry do not matter.
+ *
+ * Built for head_dim 64 and 128, page_size 16, kv_dtype PKV_BF16 or PKV_F16,
+ * max_context_len up to 262144 (PKV_ERR_UNSUPPORTED otherwise).  A one-token
+ * chunk with context_lens[b] < 1 gets NaN, like any chunk longer than its
+ * context.
+ */
+int paged_attn_mixed(const void* q, int q_dtype,
+                     const void* k_cache, const void* v_cache,
+                     const float* k_scales, const float* v_scales, int kv_dtype,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* cu_q_lens,
+                     int num_tokens, int max_q_len, int max_context_len,
+                     int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                     int page_size, int num_pages, float scale,
+                     void* out, int out_dtype,
+                     void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
+/* Workspace bytes paged_attn_mixed needs (0 when no context needs splitting,
+ * or for invalid shapes).  Pure host arithmetic; touches no device. */
+size_t paged_attn_mixed_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int max_q_len, int max_context_len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                              _c_int, _vp, _c_size, _vp]
     lib.paged_attn_prefill_workspace_bytes.restype = _c_size
     lib.paged_attn_prefill_workspace_bytes.argtypes = [_c_int] * 6
+    lib.paged_attn_mixed.restype = _c_int
+    lib.paged_attn_mixed.argtypes = lib.paged_attn_prefill_chunk.argtypes
+    lib.paged_attn_mixed_workspace_bytes.restype = _c_size
+    lib.paged_attn_mixed_workspace_bytes.argtypes = [_c_int] * 6
     _lib = lib
     return lib
 
@@ -162,21 +166,44 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_conte
     return out
 
 
+def paged_attn_mixed_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_q_len,
+                                     max_context_len) -> int:
+    return int(load_library().paged_attn_mixed_workspace_bytes(
+        batch, num_q_heads, num_kv_heads, head_dim, max_q_len, max_context_len))
+
+
+def paged_attn_mixed(q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, max_q_len,
+                     max_context_len, scale, out=None, out_dtype=torch.float32, k_scales=None,
+                     v_scales=None, workspace=None, stream=None):
+    """Same arguments and result as paged_attn_prefill_chunk; one-token chunks
+    run as split decode partitions in the same launch."""
+    return _varlen("paged_attn_mixed", paged_attn_mixed_workspace_bytes, q, k_cache, v_cache,
+                   block_tables, context_lens, cu_q_lens, max_q_len, max_context_len, scale, out,
+                   out_dtype, k_scales, v_scales, workspace, stream)
+
+
 def paged_attn_prefill_chunk(q, k_cache, v_cache, block_tables, context_lens, cu_q_lens,
                              max_q_len, max_context_len, scale, out=None,
                              out_dtype=torch.float32, k_scales=None, v_scales=None,
                              workspace=None, stream=None):
     """q [T, Hq, d] -> out [T, Hq, d]; cu_q_lens int32 [B+1]; context_lens
     int32 [B] = prefix + chunk."""
+    return _varlen("paged_attn_prefill_chunk", paged_attn_prefill_workspace_bytes, q, k_cache,
+                   v_cache, block_tables, context_lens, cu_q_lens, max_q_len, max_context_len,
+                   scale, out, out_dtype, k_scales, v_scales, workspace, stream)
+
+
+def _varlen(fn, ws_query, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, max_q_len,
+            max_context_len, scale, out, out_dtype, k_scales, v_scales, workspace, stream):
     T, hq, d = q.shape
     B = int(context_lens.shape[0])
     num_pages, hkv, page, _ = k_cache.shape
     if out is None:
         out = torch.empty((T, hq, d), dtype=out_dtype, device=q.device)
     _dev(q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, out, k_scales, v_scales)
-    nbytes = paged_attn_prefill_workspace_bytes(B, hq, hkv, d, max_q_len, max_context_len)
+    nbytes = ws_query(B, hq, hkv, d, max_q_len, max_context_len)
     workspace, wbytes = _workspace(nbytes, workspace, q.device)
-    _check("paged_attn_prefill_chunk", load_library().paged_attn_prefill_chunk(
+    _check(fn, getattr(load_library(), fn)(
         _ptr(q), _code(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
         _code(k_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
         _ptr(cu_q_lens), T, int(max_q_len), int(max_context_len), B, hq, hkv, d, page,

@@ -6,7 +6,7 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip", "mixed.hip"]
 LIB = os.path.join(HERE, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

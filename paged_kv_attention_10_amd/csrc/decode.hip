@@ -6,8 +6,9 @@
 // Work split.  A workgroup of 4 waves owns one (sequence b, KV head g, tile
 // of up to 16 query heads, context split).  The context is walked in tiles
 // of 32 tokens (two pages); the tiles a split actually has are divided
-// evenly over the four waves in contiguous runs.  The page ids of a run are
-// fetched with one vector load (lane i holds the i-th page id); tiles then
+// evenly over the four waves in contiguous runs.  The split's page ids are
+// loaded into LDS in the same round trip as the context length and the
+// query (lane i of a wave then holds the i-th page id of its run); tiles
 // stream through a ring of register buffers, the next tile's loads in
 // flight while the current one computes.  Each wave keeps its own running
 // max / sum / accumulator (the max updated lazily: the accumulator is
@@ -34,110 +35,9 @@
 // converted exactly to fp16; the per-token K scale multiplies the score and
 // the per-token V scale folds into the probability.  fp32 KV uses the fp32
 // 16x16x4 MFMA.  exp is exp2 of a log2e-prescaled score.
-#include <math.h>
-
-#include <type_traits>
-
-#include "pkv_device.h"
-#include "pkv_host.h"
+#include "decode_body.h"
 
 namespace pkv {
-
-struct DecodeArgs {
-  const void* q;
-  const void* k_cache;
-  const void* v_cache;
-  const float* k_scales;
-  const float* v_scales;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  void* out;
-  float* part_o;
-  float* part_lse;
-  int q_dtype, out_dtype;
-  int max_blocks, max_context_len;
-  int batch, hq, hkv, group, head_tiles, num_pages;
-  int tiles_per_split, nsplits;
-  float scale_log2;
-};
-
-constexpr float kDecodeLazyRescale = 8.0f;
-
-// Context length as the kernels use it; flags lengths the block table
-// cannot hold.
-__device__ __forceinline__ int checked_ctx(int raw, int max_ctx, int max_blocks, bool& bad) {
-  int lim = min(max_ctx, max_blocks * kPage);
-  if (raw < 0) { bad = true; return 0; }
-  if (raw > lim) { bad = true; return lim; }
-  return raw;
-}
-
-template <int D, int KV>
-struct DecodeTile {
-  // K fragments: 16-byte loads per MFMA row-half u.
-  static constexpr int KL = (KV == PKV_F32) ? D / 16 : (KV == PKV_I8 ? D / 64 : D / 32);
-  u32x4 k[2][KL];
-  // V^T fragments, one per 16-row block of d.
-  u32x4 v[(KV == PKV_I8) ? 1 : D / 16][(KV == PKV_F32) ? 2 : 1];
-  u32x2 v8[(KV == PKV_I8) ? D / 16 : 1];
-  f32x4 ks[2], vs[2];
-};
-
-// Register ring depth: tiles in flight per wave, sized so the ring, the
-// query fragments and the accumulators stay within the VGPR budget.
-template <int D, int KV>
-constexpr int ring_depth() {
-#ifdef PKV_DECODE_RING
-  if (!(KV == PKV_F32 && D == 128)) return PKV_DECODE_RING;
-#endif
-  return (KV == PKV_F32 && D == 128) ? 1 : 2;
-}
-
-template <int D, int KV>
-__device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs& a, int g,
-                                          int pa, int pb, int lane) {
-  const int r = lane & 15, kg = lane >> 4;
-  const int page_k = (r < 8) ? pa : pb;
-  const int rows_tok = 8 * ((r >> 2) & 1) + (r & 3);  // + 4*u
-  constexpr int ES = (KV == PKV_F32) ? 4 : (KV == PKV_I8 ? 1 : 2);
-  const char* kbase = static_cast<const char*>(a.k_cache) +
-                      ((long)page_k * a.hkv + g) * (long)(kPage * D) * ES;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const char* row = kbase + (long)(rows_tok + 4 * u) * D * ES;
-#pragma unroll
-    for (int s = 0; s < DecodeTile<D, KV>::KL; ++s) {
-      int d0;
-      if constexpr (KV == PKV_F32) d0 = 16 * s + 4 * kg;
-      else if constexpr (KV == PKV_I8) d0 = 64 * s + 16 * kg;
-      else d0 = 32 * s + 8 * kg;
-      t.k[u][s] = *reinterpret_cast<const u32x4*>(row + (long)d0 * ES);
-    }
-  }
-  const int page_v = (kg < 2) ? pa : pb;
-  const char* vbase = static_cast<const char*>(a.v_cache) +
-                      ((long)page_v * a.hkv + g) * (long)(D * kPage) * ES;
-#pragma unroll
-  for (int blk = 0; blk < D / 16; ++blk) {
-    const char* p = vbase + ((long)(16 * blk + r) * kPage + 8 * (kg & 1)) * ES;
-    if constexpr (KV == PKV_I8) {
-      t.v8[blk] = *reinterpret_cast<const u32x2*>(p);
-    } else if constexpr (KV == PKV_F32) {
-      t.v[blk][0] = *reinterpret_cast<const u32x4*>(p);
-      t.v[blk][1] = *reinterpret_cast<const u32x4*>(p + 16);
-    } else {
-      t.v[blk][0] = *reinterpret_cast<const u32x4*>(p);
-    }
-  }
-  if constexpr (KV == PKV_I8) {
-    // scales of the 8 tokens 8*kg..8*kg+7 this lane holds scores for
-    const long sidx = ((long)page_v * a.hkv + g) * kPage + 8 * (kg & 1);
-    t.ks[0] = *reinterpret_cast<const f32x4*>(a.k_scales + sidx);
-    t.ks[1] = *reinterpret_cast<const f32x4*>(a.k_scales + sidx + 4);
-    t.vs[0] = *reinterpret_cast<const f32x4*>(a.v_scales + sidx);
-    t.vs[1] = *reinterpret_cast<const f32x4*>(a.v_scales + sidx + 4);
-  }
-}
 
 #ifndef PKV_DECODE_MIN_WAVES
 #define PKV_DECODE_MIN_WAVES 2
@@ -145,352 +45,8 @@ __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs
 
 template <int D, int KV>
 __global__ __launch_bounds__(64 * kDecodeWaves, PKV_DECODE_MIN_WAVES) void decode_partition_kernel(DecodeArgs a) {
-  constexpr bool kF32 = (KV == PKV_F32);
-  constexpr bool kI8 = (KV == PKV_I8);
-  constexpr bool kBF16 = (KV == PKV_BF16);
-  using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
-  constexpr int NSTEP = kF32 ? D / 4 : D / 32;    // QK MFMA k-steps
-  constexpr int NBLK = D / 16;
-  constexpr int R = ring_depth<D, KV>();
-
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / a.head_tiles;
-  const int ht = blockIdx.y % a.head_tiles;
-  const int b = blockIdx.z;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 15;
-  const int j = lane >> 4;
-  const int h0 = g * a.group + ht * 16;
-  const int nh = min(16, a.group - ht * 16);
-
-  // ---- one round trip for the context length, the query and the page ids
-  //      of the whole split (loaded before the context length says which of
-  //      them the split uses and how its tiles divide over the waves; entries
-  //      past the context are never used)
-  const int raw_ctx = a.context_lens[b];
-  __shared__ int s_pid[2 * kDecodeMaxTilesPerSplit];
-  {
-    const int sp0 = 2 * split * a.tiles_per_split;          // the split's first page
-    const int i = threadIdx.x;
-    if (i < 2 * a.tiles_per_split && sp0 + i < a.max_blocks)
-      s_pid[i] = a.block_tables[(long)b * a.max_blocks + sp0 + i];
-  }
-
-  float qf[kF32 ? NSTEP : 1];
-  H8 qhi[kF32 ? 1 : NSTEP], qlo[kF32 ? 1 : NSTEP];
-  {
-    const long qrow = ((long)b * a.hq + h0 + c) * D;
-    const bool live = c < nh;
-    if constexpr (kF32) {
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        int d = 16 * (s >> 2) + 4 * j + (s & 3);
-        qf[s] = live ? load_as_f32(a.q, qrow + d, a.q_dtype) : 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        int d0 = kI8 ? (64 * (s >> 1) + 16 * j + 8 * (s & 1)) : (32 * s + 8 * j);
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? load_as_f32(a.q, qrow + d0 + e, a.q_dtype) : 0.f;
-        if constexpr (kBF16) {
-          auto sp = split_bf16(x);
-          qhi[s] = sp.hi;
-          qlo[s] = sp.lo;
-        } else {
-          auto sp = split_f16(x);
-          qhi[s] = sp.hi;
-          qlo[s] = sp.lo;
-        }
-      }
-    }
-  }
-
-  bool bad = false;
-  const int ctx = checked_ctx(raw_ctx, a.max_context_len, a.max_blocks, bad);
-  const int ntiles = (ctx + 31) >> 5;
-  const int nsplit_b = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  if (split >= (nsplit_b > 0 ? nsplit_b : 1)) return;
-  const int npages = (ctx + kPage - 1) / kPage;
-  // the split's tiles, divided evenly over the waves in contiguous runs
-  const int st0 = split * a.tiles_per_split;
-  const int stn = max(0, min(ntiles - st0, a.tiles_per_split));
-  const int per = (stn + kDecodeWaves - 1) / kDecodeWaves;   // <= 32
-  const int wt0 = st0 + wave * per;                          // first tile of the wave
-  const int ntw = max(0, min(st0 + stn - wt0, per));
-  const int wp0 = 2 * wt0;                                   // its first page
-  const int npw = max(0, min(npages - wp0, 2 * ntw));
-  __syncthreads();   // the split's page ids are in LDS
-  int pid = 0;
-  if (lane < npw) {
-    pid = s_pid[wp0 - 2 * st0 + lane];
-    if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
-  }
-
-  f32x4 acc[NBLK];
-#pragma unroll
-  for (int i = 0; i < NBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-
-  auto issue = [&](DecodeTile<D, KV>& dst, int li) {
-    const int pa = __builtin_amdgcn_readlane(pid, 2 * li);
-    const int pb = (2 * li + 1 < npw) ? __builtin_amdgcn_readlane(pid, 2 * li + 1) : pa;
-    load_tile<D, KV>(dst, a, g, pa, pb, lane);
-  };
-
-  auto compute = [&](const DecodeTile<D, KV>& cur, int li) {
-    // ---- S^T = K * Q^T for the 32 tile tokens
-    f32x4 s2[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kF32) {
-#pragma unroll
-        for (int s4 = 0; s4 < D / 16; ++s4) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sacc = mfma16x16x4(__uint_as_float(cur.k[u][s4][e]), qf[4 * s4 + e], sacc);
-        }
-      } else if constexpr (kI8) {
-#pragma unroll
-        for (int s2i = 0; s2i < D / 64; ++s2i) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            f16x8 kf;
-            i8x8_to_f16x8(u32x2{cur.k[u][s2i][2 * h], cur.k[u][s2i][2 * h + 1]}, kf);
-            sacc = mfma16x16x32(kf, qhi[2 * s2i + h], sacc);
-            sacc = mfma16x16x32(kf, qlo[2 * s2i + h], sacc);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < NSTEP; ++s) {
-          H8 kf = __builtin_bit_cast(H8, cur.k[u][s]);
-          sacc = mfma16x16x32(kf, qhi[s], sacc);
-          sacc = mfma16x16x32(kf, qlo[s], sacc);
-        }
-      }
-      s2[u] = sacc;
-    }
-
-    // ---- scores of head c for tile tokens 8j + e, e = 4u + i; only the
-    //      tile holding the context end needs masking
-    const int t = wt0 + li;
-    const int tok0 = 32 * t + 8 * j;
-    const bool partial = (32 * t + 32 > ctx);
-    float sc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = s2[e >> 2][e & 3] * a.scale_log2;
-      if constexpr (kI8) x *= cur.ks[e >> 2][e & 3];
-      sc[e] = x;
-    }
-    if (partial) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (tok0 + e >= ctx) sc[e] = -INFINITY;
-    }
-    float mt = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
-    mt = wave_max_xor_16_32(mt);
-    // lazy running max: the accumulator is rescaled only when the max grows
-    // by more than 2^8; the stale max cancels in the final normalisation
-    if (__any(mt > m_run + kDecodeLazyRescale)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int i = 0; i < NBLK; ++i) acc[i] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float p[8];
-    float lsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
-      lsum += p[e];
-    }
-    l_part += lsum;
-
-    // ---- O^T += V^T * P^T
-    if constexpr (kF32) {
-#pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float v = __uint_as_float(cur.v[blk][e >> 2][e & 3]);
-          if (partial && tok0 + e >= ctx) v = 0.f;
-          acc[blk] = mfma16x16x4(v, p[e], acc[blk]);
-        }
-      }
-    } else {
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = p[e];
-        if constexpr (kI8) x = (tok0 + e < ctx) ? x * cur.vs[e >> 2][e & 3] : 0.f;
-        pv[e] = x;
-      }
-      // V of tokens at or past the context end may hold anything: zero them
-      u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
-      if (partial) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (tok0 + e >= ctx) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-      }
-      H8 phi, plo;
-      if constexpr (kBF16) {
-        auto sp = split_bf16(pv);
-        phi = sp.hi;
-        plo = sp.lo;
-      } else {
-        auto sp = split_f16(pv);
-        phi = sp.hi;
-        plo = sp.lo;
-      }
-#pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) {
-        H8 vf;
-        if constexpr (kI8) {
-          f16x8 tmp;
-          i8x8_to_f16x8(cur.v8[blk], tmp);
-          vf = tmp;
-        } else {
-          u32x4 wv = cur.v[blk][0];
-          if (partial) wv &= vmask;
-          vf = __builtin_bit_cast(H8, wv);
-        }
-        acc[blk] = mfma16x16x32(vf, phi, acc[blk]);
-        acc[blk] = mfma16x16x32(vf, plo, acc[blk]);
-      }
-    }
-  };
-
-  // ---- stream the wave's tiles through the register ring
-  DecodeTile<D, KV> ring[R];
-#pragma unroll
-  for (int r = 0; r < R - 1; ++r)
-    if (r < ntw) issue(ring[r], r);
-  for (int i0 = 0; i0 < ntw; i0 += R) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = i0 + r;
-      if (i < ntw) {
-        if (i + R - 1 < ntw) issue(ring[(r + R - 1) % R], i + R - 1);
-        compute(ring[r], i);
-      }
-    }
-  }
-  const float l_run = wave_sum_xor_16_32(l_part);
-
-  // ---- merge the four waves in LDS
-  __shared__ float s_m[kDecodeWaves][16];
-  __shared__ float s_l[kDecodeWaves][16];
-  __shared__ float s_o[kDecodeWaves][16][D + 1];
-  __shared__ int s_bad;
-  if (threadIdx.x == 0) s_bad = 0;
-  __syncthreads();
-  if (bad) atomicOr(&s_bad, 1);
-  if (j == 0) {
-    s_m[wave][c] = m_run;
-    s_l[wave][c] = l_run;
-  }
-#pragma unroll
-  for (int blk = 0; blk < NBLK; ++blk) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[wave][c][16 * blk + 4 * j + i] = acc[blk][i];
-  }
-  __syncthreads();
-  const bool any_bad = s_bad != 0;
-  const bool direct = nsplit_b <= 1;
-  for (int idx = threadIdx.x; idx < nh * D; idx += 64 * kDecodeWaves) {
-    const int hc = idx / D, d = idx - hc * D;
-    float M = s_m[0][hc];
-#pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][hc]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        float f = __builtin_amdgcn_exp2f(s_m[w][hc] - M);
-        num += s_o[w][hc][d] * f;
-        den += s_l[w][hc] * f;
-      }
-    }
-    float val = den > 0.f ? num / den : 0.f;
-    if (any_bad) val = NAN;
-    const long row = (long)b * a.hq + h0 + hc;
-    if (direct) {
-      store_from_f32(a.out, row * D + d, a.out_dtype, val);
-    } else {
-      const long prow = row * a.nsplits + split;
-      a.part_o[prow * D + d] = val;
-      if (d == 0) a.part_lse[prow] = any_bad ? NAN : (den > 0.f ? M + log2f(den) : -INFINITY);
-    }
-  }
-}
-
-// Log-sum-exp merge of the split partials of one (sequence, query head):
-// out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
-// One wave per row; the context length, every split's lse and every
-// partial element this lane needs are loaded together, so the merge costs
-// one memory round trip.  Rows whose sequence fit one split were written by
-// the partition kernel and are skipped.
-template <int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
-  constexpr int PER = D / 64;
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const long row = (long)b * a.hq + h;
-  const int S = a.nsplits;                       // <= kDecodeMaxSplits
-  const int raw_ctx = a.context_lens[b];
-  const float lse_l = lane < S ? a.part_lse[row * S + lane] : -INFINITY;
-  float o[kDecodeMaxSplits][PER];
-#pragma unroll
-  for (int s = 0; s < kDecodeMaxSplits; ++s) {
-    if (s < S) {
-#pragma unroll
-      for (int e = 0; e < PER; ++e) o[s][e] = a.part_o[(row * S + s) * D + lane + 64 * e];
-    }
-  }
-  bool bad = false;
-  const int ctx = checked_ctx(raw_ctx, a.max_context_len, a.max_blocks, bad);
-  const int ntiles = (ctx + 31) >> 5;
-  const int ns = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  if (ns <= 1) return;
-  const float mine = lane < ns ? lse_l : -INFINITY;
-  float M = mine;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
-  const float w_l = (M == -INFINITY || lane >= ns) ? 0.f : __builtin_amdgcn_exp2f(mine - M);
-  float den = w_l;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m);
-  // a NaN partial (a split that met a bad page id) poisons the row
-  const bool nan_in = __any(mine != mine);
-  float num[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.f;
-#pragma unroll
-  for (int s = 0; s < kDecodeMaxSplits; ++s) {
-    if (s < ns) {
-      const float w = __shfl(w_l, s);
-#pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] += o[s][e] * w;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    float val = den > 0.f ? num[e] / den : 0.f;
-    if (bad || nan_in) val = NAN;
-    store_from_f32(a.out, row * D + lane + 64 * e, a.out_dtype, val);
-  }
+  __shared__ __attribute__((aligned(16))) char smem[DecodeSmem<D>::total];
+  decode_partition_body<D, KV>(a, smem, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 template <int D, int KV>
@@ -565,6 +121,7 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
   a.v_scales = v_scales;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.cu_q_lens = nullptr;
   a.out = out;
   char* wsb = static_cast<char*>(workspace);
   a.part_o = ws.total ? reinterpret_cast<float*>(wsb + ws.part_o_offset) : nullptr;

@@ -1,0 +1,173 @@
+// Mixed batch: prefill chunks and decode tokens in one varlen call
+// (Tiny-LLM "Project Status", supported features: chunked prefill/decode
+// scheduling over a paged KV cache; TinyLoop "Current Status", table "Model
+// architecture support", row "Chunked prefill").  The semantics are those of
+// paged_attn_prefill_chunk: chunk row i of sequence b sits at position
+// P_b + i and attends to [0, P_b + i]; a decode token is a chunk of one.
+//
+// One launch holds two kinds of workgroups.  The first part of the grid is
+// the prefill kernel's row blocks (heaviest first); sequences whose chunk is
+// a single token leave them empty.  The second part is the decode kernel's
+// split partitions, which take exactly those single-token sequences (their
+// query and output rows mapped through cu_q_lens), so a decode token's
+// context is cut across several workgroups instead of walked by one.  Both
+// kinds share the workgroup's LDS buffer and its register budget; the
+// decode splits are merged by the decode reduce kernel afterwards.
+#include "decode_body.h"
+#include "prefill_body.h"
+
+namespace pkv {
+
+template <int D>
+constexpr int mixed_lds_bytes() {
+  return 2 * PrefillLds<D>::stage > DecodeSmem<D>::total ? 2 * PrefillLds<D>::stage
+                                                         : DecodeSmem<D>::total;
+}
+
+static_assert(64 * kDecodeWaves == 256, "both kinds of workgroup have 256 threads");
+
+template <int D, int KV, bool QSPLIT>
+__global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs da, PrefillArgs pa, int n_prefill) {
+  __shared__ __attribute__((aligned(1024))) char lds[mixed_lds_bytes<D>()];
+  const int id = blockIdx.x;
+  if (id < n_prefill) {
+    const int b = id % pa.batch, r = id / pa.batch;
+    prefill_body<D, KV, QSPLIT>(pa, lds, b, r % pa.hkv, pa.nrowblocks - 1 - r / pa.hkv);
+  } else {
+    const int j = id - n_prefill;
+    const int ny = da.hkv * da.head_tiles;
+    const int split = j % da.nsplits, r = j / da.nsplits;
+    decode_partition_body<D, KV>(da, lds, split, r % ny, r / ny);
+  }
+}
+
+template <int D, int KV>
+static void launch_mixed(const DecodeArgs& da, const PrefillArgs& pa, int n_prefill, int n_decode,
+                         pkv_stream_t stream) {
+  const dim3 grid(n_prefill + n_decode);
+  if (pa.q_dtype == KV)
+    hipLaunchKernelGGL((mixed_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, da, pa,
+                       n_prefill);
+  else
+    hipLaunchKernelGGL((mixed_kernel<D, KV, true>), grid, dim3(256), 0, (hipStream_t)stream, da, pa,
+                       n_prefill);
+  if (da.nsplits > 1)
+    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(da.hq, da.batch), dim3(64), 0,
+                       (hipStream_t)stream, da);
+}
+
+template <int D>
+static void dispatch_mixed(int kv, const DecodeArgs& da, const PrefillArgs& pa, int n_prefill,
+                           int n_decode, pkv_stream_t stream) {
+  if (kv == PKV_BF16) launch_mixed<D, PKV_BF16>(da, pa, n_prefill, n_decode, stream);
+  else launch_mixed<D, PKV_F16>(da, pa, n_prefill, n_decode, stream);
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" size_t paged_attn_mixed_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
+                                                   int head_dim, int max_q_len, int max_context_len) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      !head_dim_built(head_dim) || max_q_len < 0 || max_context_len < 0 ||
+      (long)max_context_len > kDecodeMaxContext)
+    return 0;
+  const DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+  return decode_workspace_layout(batch, num_q_heads, head_dim, p).total;
+}
+
+extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                                const float* k_scales, const float* v_scales, int kv_dtype,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* cu_q_lens,
+                                int num_tokens, int max_q_len, int max_context_len, int batch,
+                                int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                                int num_pages, float scale, void* out, int out_dtype,
+                                void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens ||
+      ((!q || !out) && num_tokens > 0))
+    return PKV_ERR_INVALID_ARG;
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      num_pages <= 0 || max_blocks_per_seq <= 0 || num_tokens < 0 || max_q_len < 0 ||
+      max_context_len < 0 || max_q_len > max_context_len || batch > 65535 ||
+      (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE)
+    return PKV_ERR_INVALID_ARG;
+  if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
+    return PKV_ERR_INVALID_ARG;
+  if ((kv_dtype == PKV_I8) != (k_scales != nullptr) || (kv_dtype == PKV_I8) != (v_scales != nullptr))
+    return PKV_ERR_INVALID_ARG;
+  if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim) ||
+      (long)max_context_len > kDecodeMaxContext)
+    return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16) return PKV_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(block_tables) || !aligned16(context_lens) || !aligned16(cu_q_lens))
+    return PKV_ERR_MISALIGNED;
+  if (num_tokens == 0 || max_q_len == 0) return PKV_OK;
+
+  const DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+  const DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, head_dim, p);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace && !aligned16(workspace)) return PKV_ERR_MISALIGNED;
+
+  DecodeArgs da;
+  da.q = q;
+  da.k_cache = k_cache;
+  da.v_cache = v_cache;
+  da.k_scales = nullptr;
+  da.v_scales = nullptr;
+  da.block_tables = block_tables;
+  da.context_lens = context_lens;
+  da.cu_q_lens = cu_q_lens;
+  da.out = out;
+  char* wsb = static_cast<char*>(workspace);
+  da.part_o = ws.total ? reinterpret_cast<float*>(wsb + ws.part_o_offset) : nullptr;
+  da.part_lse = ws.total ? reinterpret_cast<float*>(wsb + ws.part_lse_offset) : nullptr;
+  da.q_dtype = q_dtype;
+  da.out_dtype = out_dtype;
+  da.max_blocks = max_blocks_per_seq;
+  da.max_context_len = max_context_len;
+  da.batch = batch;
+  da.hq = num_q_heads;
+  da.hkv = num_kv_heads;
+  da.group = num_q_heads / num_kv_heads;
+  da.head_tiles = p.head_tiles;
+  da.num_pages = num_pages;
+  da.tiles_per_split = p.tiles_per_split;
+  da.nsplits = p.nsplits;
+  da.scale_log2 = scale * kLog2e;
+
+  PrefillArgs pa;
+  pa.q = q;
+  pa.k_cache = k_cache;
+  pa.v_cache = v_cache;
+  pa.block_tables = block_tables;
+  pa.context_lens = context_lens;
+  pa.cu_q_lens = cu_q_lens;
+  pa.out = out;
+  pa.q_dtype = q_dtype;
+  pa.out_dtype = out_dtype;
+  pa.max_blocks = max_blocks_per_seq;
+  pa.max_context_len = max_context_len;
+  pa.max_q_len = max_q_len;
+  pa.batch = batch;
+  pa.hq = num_q_heads;
+  pa.hkv = num_kv_heads;
+  pa.group = num_q_heads / num_kv_heads;
+  pa.num_pages = num_pages;
+  pa.nrowblocks = ceil_div((long)max_q_len * pa.group, kPrefillRowsPerBlock);
+  pa.scale_log2 = scale * kLog2e;
+  pa.skip_single = 1;
+  if (pa.nrowblocks > 65535) return PKV_ERR_INVALID_ARG;
+
+  // no row block can hold work when every chunk has at most one token
+  const long n_prefill = max_q_len > 1 ? (long)batch * num_kv_heads * pa.nrowblocks : 0;
+  const long n_decode = (long)p.nsplits * num_kv_heads * p.head_tiles * batch;
+  if (n_prefill + n_decode > 0x7fffffffL) return PKV_ERR_INVALID_ARG;
+
+  clear_launch_error();
+  if (head_dim == 64) dispatch_mixed<64>(kv_dtype, da, pa, (int)n_prefill, (int)n_decode, stream);
+  else dispatch_mixed<128>(kv_dtype, da, pa, (int)n_prefill, (int)n_decode, stream);
+  return launch_status();
+}

@@ -25,7 +25,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {
         "pkv_abi_version", "pkv_status_string", "paged_kv_append", "paged_attn_decode",
         "paged_attn_decode_workspace_bytes", "paged_attn_prefill_chunk",
-        "paged_attn_prefill_workspace_bytes"}
+        "paged_attn_prefill_workspace_bytes", "paged_attn_mixed", "paged_attn_mixed_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -69,6 +69,14 @@ def _prefill(lib, **over):
     return lib.paged_attn_prefill_chunk(*a.values())
 
 
+def _mixed(lib, **over):
+    a = dict(q=FAKE, qd=1, k=FAKE, v=FAKE, ks=None, vs=None, kvd=1, bt=FAKE, mb=8, cl=FAKE,
+             cu=FAKE, T=64, mql=32, mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125,
+             out=FAKE, od=0, ws=FAKE, wsb=1 << 20, st=None)
+    a.update(over)
+    return lib.paged_attn_mixed(*a.values())
+
+
 def _append(lib, **over):
     a = dict(k=FAKE, v=FAKE, nd=0, slots=FAKE, T=4, kc=FAKE, vc=FAKE, ks=None, vs=None, cd=1,
              np_=32, hkv=2, d=64, ps=16, st=None)
@@ -110,6 +118,30 @@ def test_decode_rejects(lib, over, code):
 ])
 def test_prefill_rejects(lib, over, code):
     assert _prefill(lib, **over) == code
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    ({"cu": None}, INVALID), ({"bt": None}, INVALID), ({"mql": 200}, INVALID), ({"T": -1}, INVALID),
+    ({"hq": 3}, INVALID), ({"mcl": 200}, INVALID), ({"B": 70000}, INVALID),
+    ({"kvd": 0}, UNSUPPORTED), ({"kvd": 3, "ks": FAKE, "vs": FAKE}, UNSUPPORTED),
+    ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED),
+    ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest split context
+    ({"cu": FAKE + 4}, MISALIGNED), ({"od": 3}, INVALID),
+    ({"mcl": 4096, "mb": 256, "B": 64, "hq": 12, "hkv": 2, "d": 128, "ws": None, "wsb": 0}, WS_SMALL),
+])
+def test_mixed_rejects(lib, over, code):
+    assert _mixed(lib, **over) == code
+
+
+def test_mixed_workspace_is_the_decode_split_workspace(lib):
+    ws = lib.paged_attn_mixed_workspace_bytes
+    assert ws(64, 12, 2, 128, 512, 4096) == lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096) > 0
+    assert ws(0, 12, 2, 128, 512, 4096) == 0
+
+
+def test_mixed_empty_call_is_noop(lib):
+    assert _mixed(lib, T=0, q=None, out=None) == 0
 
 
 @pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
