@@ -42,6 +42,8 @@ DESC = {
     "C3": "paged decode, fp16 KV, Stories110M shape: batch 384, 12 q / 12 KV heads, head_dim 64, ctx U[64,1024]",
     "C4": "chunked causal prefill, bf16 q/KV, Qwen2.5-1.5B shape: 8 x 512-token chunks over prefixes U[0,3584], 12 q / 2 KV heads, head_dim 128",
     "C5": "paged decode, int8 KV + per-token-head fp32 scales, TinyLlama-1.1B shape: batch 128, 32 q / 4 KV heads, head_dim 64, ctx 2048",
+    "M1": "mixed batch in one call: the C2 decode batch (64 one-token chunks, ctx U[512,4096]) and the C4 chunks (8 x 512 tokens), 12 q / 2 KV heads, head_dim 128, bf16",
+    "M2": "decode-heavy mixed batch in one call: the C2 decode batch (64 one-token chunks, ctx U[512,4096]) and 4 chunks of 64 tokens over 1024-token prefixes, 12 q / 2 KV heads, head_dim 128, bf16",
 }
 
 
@@ -255,8 +257,71 @@ def bench_prefill(g: Gpu, steps: int, warmup: int):
                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": res["tflops_prefill_call"] / BF16_PEAK_TFLOPS,
                        "traffic": profiled_traffic("prefill_C4_counters.txt",
-                                                   source_sha("prefill.hip", "pkv_device.h", "pkv_host.h"))}
+                                                   source_sha("prefill.hip", "prefill_body.h", "pkv_device.h", "pkv_host.h"))}
     return w, res, out
+
+
+def mixed_workload(name):
+    """M1: C2's 64 decode sequences and C4's eight 512-token chunks in one
+    batch.  M2 (decode-heavy): C2's 64 decode sequences and four 64-token
+    chunks over 1024-token prefixes.  Same heads, head_dim 128, bf16 q and
+    KV, seeded draw."""
+    from workloads import custom_workload, make_workload
+    w2 = make_workload("C2")
+    if name == "M1":
+        w4 = make_workload("C4")
+        chunks = [(int(c), int(q)) for c, q in zip(w4.context_lens, w4.q_lens)]
+    else:
+        chunks = [(1024 + 64, 64)] * 4
+    ctx = [int(x) for x in w2.context_lens] + [c for c, _ in chunks]
+    q_lens = [1] * w2.batch + [q for _, q in chunks]
+    return custom_workload(kind="prefill", context_lens=ctx, q_lens=q_lens, num_q_heads=12,
+                           num_kv_heads=2, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
+                           num_pages=20000, table_width=256, seed=6 if name == "M1" else 7,
+                           name=name)
+
+
+def bench_mixed(g: Gpu, name: str, steps: int, warmup: int):
+    w = mixed_workload(name)
+    log(f"[bench] {name}: building the pool on the GPU")
+    pool = g.pool(w)
+    g.fill_pool(w, pool, g.torch.arange(len(w.slot_mapping)).numpy())
+    k, v, _, _ = pool
+    q = g.t(w.q).to(g.torch.bfloat16)
+    bt, cl, cu = g.t(w.block_tables), g.t(w.context_lens), g.t(w.cu_q_lens)
+    out = g.torch.empty((w.num_query_tokens, w.num_q_heads, w.head_dim), dtype=g.torch.float32,
+                        device=g.dev)
+    nws = g.pkv.paged_attn_mixed_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads,
+                                                 w.head_dim, w.max_q_len, w.max_context_len)
+    ws = g.torch.zeros(max(nws, 16), dtype=g.torch.uint8, device=g.dev)
+
+    def mixed():
+        g.pkv.paged_attn_mixed(q, k, v, bt, cl, cu, w.max_q_len, w.max_context_len, w.scale,
+                               out=out, workspace=ws)
+
+    def prefill_only():
+        g.pkv.paged_attn_prefill_chunk(q, k, v, bt, cl, cu, w.max_q_len, w.max_context_len,
+                                       w.scale, out=out)
+
+    def step(inner, e1=None, e2=None):
+        if e1 is not None:
+            e1.record()
+        inner()
+        if e2 is not None:
+            e2.record()
+
+    log(f"[bench] {name}: {warmup} warmup + {steps} timed steps, mixed and prefill-only calls")
+    _, mixed_ms, _ = g.timed_steps(step, mixed, steps, warmup)
+    _, pre_ms, _ = g.timed_steps(step, prefill_only, steps, warmup)
+    sm, sp = stats(mixed_ms), stats(pre_ms)
+    return {
+        "workload": name, "desc": DESC[name],
+        "mixed_call_ms": sm, "prefill_chunk_call_ms": sp,
+        "speedup_vs_prefill_chunk": sp["mean"] / sm["mean"],
+        "query_tokens_per_s": w.num_query_tokens / (sm["mean"] * 1e-3),
+        "decode_tokens": 64, "prefill_tokens": int(w.num_query_tokens) - 64,
+        "plan_workspace_bytes": int(nws),
+    }
 
 
 def cpu_baseline(w, gpu_out, budget_s: float):
@@ -307,13 +372,13 @@ def main():
                     help="seconds of oracle CPU work for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of workloads to run (C1..C5); default all")
+                    help="comma list of workloads to run (C1..C5, M1, M2); default all")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5"}
+    only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2"}
 
     g = Gpu()
     extras = {}
@@ -326,11 +391,14 @@ def main():
             r["roofline"] = {"bound": "hbm", "achieved": r["decode_call_gbs"], "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": r["decode_call_gbs"] / HBM_PEAK_GBS,
                              "traffic": profiled_traffic(f"decode_{name}_counters.txt",
-                                                         source_sha("decode.hip", "pkv_device.h", "pkv_host.h"))}
+                                                         source_sha("decode.hip", "decode_body.h", "pkv_device.h", "pkv_host.h"))}
             extras[f"decode_{name}"] = r
     if "C4" in only:
         _, rp, _ = bench_prefill(g, args.steps, args.warmup)
         extras["prefill_C4"] = rp
+    for name in ("M1", "M2"):
+        if name in only:
+            extras[f"mixed_{name}"] = bench_mixed(g, name, args.steps, args.warmup)
 
     line = {
         "metric": "decode KV GB/s (% HBM peak) + seq-tokens/s; prefill TFLOP/s (% MFMA)",
@@ -353,7 +421,7 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(head["decode_call_gbs"] / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("decode_C2_counters.txt",
-                                                     source_sha("decode.hip", "pkv_device.h", "pkv_host.h")),
+                                                     source_sha("decode.hip", "decode_body.h", "pkv_device.h", "pkv_host.h")),
                          "kernel": "paged_attn_decode call: decode_partition_kernel<128,bf16> + decode_reduce_kernel<128>, events around both",
                          "algorithmic_bytes_per_launch": head["effective_kv_bytes"]},
             "detail_C2": head,

@@ -229,8 +229,10 @@ int paged_attn_mixed(const void* q, int q_dtype,
                      void* out, int out_dtype,
                      void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
-/* Workspace bytes paged_attn_mixed needs (0 when no context needs splitting,
- * or for invalid shapes).  Pure host arithmetic; touches no device. */
+/* Workspace bytes paged_attn_mixed needs (0 when no context is split, or for
+ * invalid shapes).  The one-token rows are split across their context as in
+ * paged_attn_decode when max_q_len < 128, and only as far as contexts beyond
+ * 4096 tokens require otherwise.  Pure host arithmetic; touches no device. */
 size_t paged_attn_mixed_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
                                         int head_dim, int max_q_len, int max_context_len);
 

@@ -8,11 +8,14 @@
 // One launch holds two kinds of workgroups.  The first part of the grid is
 // the prefill kernel's row blocks (heaviest first); sequences whose chunk is
 // a single token leave them empty.  The second part is the decode kernel's
-// split partitions, which take exactly those single-token sequences (their
-// query and output rows mapped through cu_q_lens), so a decode token's
-// context is cut across several workgroups instead of walked by one.  Both
-// kinds share the workgroup's LDS buffer and its register budget; the
-// decode splits are merged by the decode reduce kernel afterwards.
+// partitions, which take exactly those single-token sequences (their query
+// and output rows mapped through cu_q_lens): a decode token is walked by
+// four waves with 16-query-head MFMA tiles instead of occupying a 128-row
+// prefill block.  When the batch holds only short chunks the one-token rows
+// are split across the context as in paged_attn_decode; with long chunks
+// present they take the fewest splits their context allows.  Both kinds share the
+// workgroup's LDS buffer and its register budget; split partials are merged
+// by the decode reduce kernel afterwards.
 #include "decode_body.h"
 #include "prefill_body.h"
 
@@ -63,6 +66,19 @@ static void dispatch_mixed(int kv, const DecodeArgs& da, const PrefillArgs& pa, 
   else launch_mixed<D, PKV_F16>(da, pa, n_prefill, n_decode, stream);
 }
 
+// Split plan of the one-token rows.  With long chunks in the batch
+// (max_q_len >= kMixedLongChunk) the prefill row blocks set the critical
+// path, so the one-token rows take the fewest splits their context allows (a
+// split would only add the merge launch); otherwise the one-token rows
+// dominate and are planned as a decode call.
+constexpr int kMixedLongChunk = 128;
+static DecodePlan mixed_plan(int batch, int num_q_heads, int num_kv_heads, int max_q_len,
+                             int max_context_len) {
+  return max_q_len >= kMixedLongChunk
+             ? plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, 0)
+             : plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -73,8 +89,9 @@ extern "C" size_t paged_attn_mixed_workspace_bytes(int batch, int num_q_heads, i
       !head_dim_built(head_dim) || max_q_len < 0 || max_context_len < 0 ||
       (long)max_context_len > kDecodeMaxContext)
     return 0;
-  const DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
-  return decode_workspace_layout(batch, num_q_heads, head_dim, p).total;
+  return decode_workspace_layout(batch, num_q_heads, head_dim,
+                                 mixed_plan(batch, num_q_heads, num_kv_heads, max_q_len,
+                                            max_context_len)).total;
 }
 
 extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
@@ -106,7 +123,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
     return PKV_ERR_MISALIGNED;
   if (num_tokens == 0 || max_q_len == 0) return PKV_OK;
 
-  const DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+  const DecodePlan p = mixed_plan(batch, num_q_heads, num_kv_heads, max_q_len, max_context_len);
   const DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, head_dim, p);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (workspace && !aligned16(workspace)) return PKV_ERR_MISALIGNED;

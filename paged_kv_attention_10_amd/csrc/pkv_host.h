@@ -49,13 +49,17 @@ constexpr long kDecodeMaxContext = (long)kDecodeMaxSplits * kDecodeMaxTilesPerSp
 #endif
 constexpr long kDecodeTargetWorkgroups = PKV_DECODE_TARGET_WORKGROUPS;
 
-inline DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len) {
+// target_workgroups = 0 asks for the fewest splits the context allows (a
+// mixed batch, where the prefill row blocks set the critical path and a
+// decode split would only add the merge).
+inline DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len,
+                              long target_workgroups = kDecodeTargetWorkgroups) {
   DecodePlan p;
   int group = num_q_heads / num_kv_heads;
   p.head_tiles = ceil_div(group, 16);
   int tiles_max = max_context_len > 0 ? ceil_div(max_context_len, kDecodeTileTokens) : 1;
   long units = (long)batch * num_kv_heads * p.head_tiles;
-  long want = (kDecodeTargetWorkgroups + units - 1) / units;
+  long want = (target_workgroups + units - 1) / units;
   if (want < 1) want = 1;
   int tps = ceil_div(tiles_max, want);
   tps = ceil_div(tps, kDecodeWaves) * kDecodeWaves;

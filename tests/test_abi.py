@@ -128,15 +128,21 @@ def test_prefill_rejects(lib, over, code):
     ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED),
     ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest split context
     ({"cu": FAKE + 4}, MISALIGNED), ({"od": 3}, INVALID),
-    ({"mcl": 4096, "mb": 256, "B": 64, "hq": 12, "hkv": 2, "d": 128, "ws": None, "wsb": 0}, WS_SMALL),
+    ({"mcl": 4096, "mb": 256, "B": 64, "hq": 12, "hkv": 2, "d": 128, "mql": 1, "ws": None, "wsb": 0},
+     WS_SMALL),
 ])
 def test_mixed_rejects(lib, over, code):
     assert _mixed(lib, **over) == code
 
 
-def test_mixed_workspace_is_the_decode_split_workspace(lib):
+def test_mixed_workspace_follows_the_split_plan(lib):
     ws = lib.paged_attn_mixed_workspace_bytes
-    assert ws(64, 12, 2, 128, 512, 4096) == lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096) > 0
+    # short chunks only: the one-token rows are planned as a decode call
+    dec = lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096)
+    assert ws(64, 12, 2, 128, 1, 4096) == ws(64, 12, 2, 128, 127, 4096) == dec > 0
+    # with long chunks: the fewest splits the context allows (none up to 4096 tokens)
+    assert ws(72, 12, 2, 128, 512, 4096) == 0
+    assert ws(8, 12, 2, 128, 512, 20000) > 0
     assert ws(0, 12, 2, 128, 512, 4096) == 0
 
 
