@@ -172,6 +172,53 @@ def ref_append(cache: PagedCache, k_new, v_new, slot_mapping) -> None:
         cache.v[page, :, :, off] = storage_from_f32(v_new, cache.dtype)
 
 
+def rope_f64(x, positions, theta, style: str = "half") -> np.ndarray:
+    """Rotary position embedding, float64 and unrounded.
+
+    RoPE with a configurable base theta runs in every forward path (TinyLoop
+    "Current Status", table "Model architecture support", row "RoPE"); the
+    runtimes serve LLaMA/SmolLM2-compatible and Qwen2-family checkpoints
+    (Tiny-LLM "Project Status", supported models).  The rotation follows its
+    published definition (RoFormer, Su et al. 2021): the d/2 coordinate pairs of a head vector are
+    rotated in their planes, pair i by the angle ``pos * theta**(-2 i / d)``,
+    ``(a, b) -> (a cos - b sin, b cos + a sin)``.  style "half" pairs
+    coordinate i with i + d/2 (the pairing of the Llama and Qwen reference
+    implementations); "interleaved" pairs 2i with 2i + 1.
+
+    x [T, H, d]; positions [T] integers; theta the base (taken at the fp32
+    value the library receives)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    i = np.arange(h, dtype=np.float64)
+    inv_freq = np.float64(np.float32(theta)) ** (-2.0 * i / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    if style == "half":
+        a, b = x[..., :h], x[..., h:]
+    elif style == "interleaved":
+        a, b = x[..., 0::2], x[..., 1::2]
+    else:
+        raise ValueError(style)
+    ra = a * c - b * s
+    rb = b * c + a * s
+    out = np.empty_like(x)
+    if style == "half":
+        out[..., :h], out[..., h:] = ra, rb
+    else:
+        out[..., 0::2], out[..., 1::2] = ra, rb
+    return out
+
+
+def ref_append_rope(cache: PagedCache, k_new, v_new, slot_mapping, positions, theta,
+                    style: str = "half") -> None:
+    """Append with RoPE applied to K first: the rotation is evaluated in
+    float64 and rounded to float32, then K and V are stored as ref_append
+    stores them (V is not rotated)."""
+    k_rot = rope_f64(np.asarray(k_new, dtype=np.float32), positions, theta, style)
+    ref_append(cache, k_rot.astype(np.float32), v_new, slot_mapping)
+
+
 def gather_sequence(cache: PagedCache, block_row, n: int):
     """Contiguous float64 K, V [n, Hkv, d] of one sequence's first n tokens."""
     t = np.arange(n)

@@ -367,4 +367,96 @@ def pin_append_layout(O):
         assert np.all(ci.k[s // PS, :, s % PS, :] == 0) and np.all(ci.v_scales[s // PS, :, s % PS] == 0)
 
 
+# ------------------------------------------------------------------ RoPE
+def _unit(d, i):
+    x = np.zeros((1, 1, d), dtype=np.float32)
+    x[0, 0, i] = 1.0
+    return x
+
+
+def pin_rope_golden_angles(O):
+    """Hand-derived angles: with theta = 10^4 and d = 8 the four pairs turn at
+    1, 1/10, 1/100, 1/1000 rad per position, so position 1000 turns them by
+    1000, 100, 10 and 1 rad; with theta = 100 and d = 4 position 10 turns the
+    two pairs by 10 and 1 rad.  A unit vector on a pair's first coordinate
+    goes to (cos, sin) on (first, second); one on the second coordinate to
+    (-sin, cos) -- a rotation by +angle, as in the published definition."""
+    for d, theta, pos, angles in ((8, 1e4, 1000, (1000.0, 100.0, 10.0, 1.0)),
+                                  (4, 100.0, 10, (10.0, 1.0))):
+        for style in ("half", "interleaved"):
+            for i, ang in enumerate(angles):
+                first, second = (i, i + d // 2) if style == "half" else (2 * i, 2 * i + 1)
+                want = np.zeros(d)
+                want[first], want[second] = math.cos(ang), math.sin(ang)
+                got = O.rope_f64(_unit(d, first), [pos], theta, style)[0, 0]
+                assert np.max(np.abs(got - want)) < 1e-9, (d, style, i)
+                want = np.zeros(d)
+                want[first], want[second] = -math.sin(ang), math.cos(ang)
+                got = O.rope_f64(_unit(d, second), [pos], theta, style)[0, 0]
+                assert np.max(np.abs(got - want)) < 1e-9, (d, style, i)
+
+
+def pin_rope_group_laws(O):
+    """Position 0 is the identity, rotations compose additively in position,
+    position -m undoes m, and every coordinate pair keeps its length."""
+    rng = np.random.default_rng(71)
+    for d in (8, 64, 128):
+        x = rng.standard_normal((5, 3, d)).astype(np.float32)
+        m = np.array([0, 1, 17, 4095, 262143])
+        n = np.array([3, 0, 1000, 7, 11])
+        for style in ("half", "interleaved"):
+            assert np.array_equal(O.rope_f64(x, np.zeros(5, dtype=np.int64), 1e4, style),
+                                  x.astype(np.float64))
+            once = O.rope_f64(x, m + n, 1e4, style)
+            twice = O.rope_f64(O.rope_f64(x, m, 1e4, style), n, 1e4, style)
+            assert np.max(np.abs(once - twice)) < 1e-9
+            back = O.rope_f64(O.rope_f64(x, m, 5e5, style), -m, 5e5, style)
+            assert np.max(np.abs(back - x)) < 1e-9
+            r = O.rope_f64(x, m, 1e4, style)
+            if style == "half":
+                pn = lambda y: y[..., : d // 2] ** 2 + y[..., d // 2:] ** 2   # noqa: E731
+            else:
+                pn = lambda y: y[..., 0::2] ** 2 + y[..., 1::2] ** 2          # noqa: E731
+            assert np.max(np.abs(pn(r) - pn(x.astype(np.float64)))) < 1e-9
+
+
+def pin_rope_relative_position(O):
+    """The score between a rotated query and a rotated key depends only on the
+    distance between their positions (the property RoPE is built for)."""
+    rng = np.random.default_rng(72)
+    q = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    for style in ("half", "interleaved"):
+        ref = float(np.sum(O.rope_f64(q, [40], 1e4, style) * O.rope_f64(k, [13], 1e4, style)))
+        for shift in (1, 500, 100000):
+            got = float(np.sum(O.rope_f64(q, [40 + shift], 1e4, style) *
+                               O.rope_f64(k, [13 + shift], 1e4, style)))
+            assert abs(got - ref) < 1e-9
+
+
+def pin_append_rope(O):
+    """Append with RoPE: V lands exactly as a plain append puts it; K of a
+    token at position 0 too; K of the golden unit vector lands as the float32
+    of (cos, sin) in every storage type."""
+    w = custom_workload(context_lens=[40], num_q_heads=2, num_kv_heads=2, head_dim=8, kv_dtype="f32",
+                        num_pages=4, seed=74)
+    T = w.k.shape[0]
+    pos = np.arange(T) * 37
+    for dt in ("f32", "bf16", "f16", "i8"):
+        plain = O.PagedCache(w.num_pages, 2, 8, dt)
+        O.ref_append(plain, w.k, w.v, w.slot_mapping)
+        rot = O.PagedCache(w.num_pages, 2, 8, dt)
+        O.ref_append_rope(rot, w.k, w.v, w.slot_mapping, pos, 1e4, "half")
+        assert np.array_equal(plain.v, rot.v)
+        if dt == "i8":
+            assert np.array_equal(plain.v_scales, rot.v_scales)
+        s0 = int(w.slot_mapping[0])
+        assert np.array_equal(plain.k[s0 // PS, :, s0 % PS], rot.k[s0 // PS, :, s0 % PS])
+    c = O.PagedCache(1, 1, 8, "f32")
+    O.ref_append_rope(c, _unit(8, 1), np.zeros((1, 1, 8), np.float32), [5], [1000], 1e4, "half")
+    want = np.zeros(8, np.float32)
+    want[1], want[5] = np.float32(math.cos(100.0)), np.float32(math.sin(100.0))
+    assert np.array_equal(c.k[0, 0, 5], want)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -37,6 +37,19 @@ MUTANTS = [
     ("bf16_round_half_up", "(u + 0x7FFF + ((u >> 16) & 1)) >> 16", "(u + 0x8000) >> 16"),
     ("bf16_truncates", "(u + 0x7FFF + ((u >> 16) & 1)) >> 16", "u >> 16"),
     ("append_ignores_padding", "keep = slots >= 0", "keep = slots >= -1"),
+    ("rope_turns_backwards", "ra = a * c - b * s\n    rb = b * c + a * s",
+     "ra = a * c + b * s\n    rb = b * c - a * s"),
+    ("rope_not_a_rotation", "rb = b * c + a * s", "rb = b * c - a * s"),
+    ("rope_frequency_exponent", "(-2.0 * i / d)", "(-1.0 * i / d)"),
+    ("rope_frequency_from_d_minus_2", "(-2.0 * i / d)", "(-2.0 * i / (d - 2))"),
+    ("rope_half_reads_interleaved", "a, b = x[..., :h], x[..., h:]", "a, b = x[..., 0::2], x[..., 1::2]"),
+    ("rope_position_off_by_one", "np.asarray(positions, dtype=np.float64)[:, None]",
+     "(np.asarray(positions, dtype=np.float64)[:, None] + 1)"),
+    ("rope_rotates_v", "ref_append(cache, k_rot.astype(np.float32), v_new, slot_mapping)",
+     "ref_append(cache, k_rot.astype(np.float32), rope_f64(np.asarray(v_new, dtype=np.float32), "
+     "positions, theta, style).astype(np.float32), slot_mapping)"),
+    ("rope_f16_intermediate", "ref_append(cache, k_rot.astype(np.float32), v_new, slot_mapping)",
+     "ref_append(cache, k_rot.astype(np.float16).astype(np.float32), v_new, slot_mapping)"),
 ]
 
 
