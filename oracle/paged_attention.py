@@ -219,6 +219,15 @@ def ref_append_rope(cache: PagedCache, k_new, v_new, slot_mapping, positions, th
     ref_append(cache, k_rot.astype(np.float32), v_new, slot_mapping)
 
 
+def ref_rope_q(q, positions, theta, style: str, dtype: str) -> np.ndarray:
+    """Queries rotated as the fused append rotates them: each query row of
+    token j turns by its position, the float64 result is rounded to float32
+    and then to the query's own dtype (storage representation of
+    storage_from_f32)."""
+    rot = rope_f64(np.asarray(q, dtype=np.float32), positions, theta, style)
+    return storage_from_f32(rot.astype(np.float32), dtype)
+
+
 def gather_sequence(cache: PagedCache, block_row, n: int):
     """Contiguous float64 K, V [n, Hkv, d] of one sequence's first n tokens."""
     t = np.arange(n)

@@ -457,6 +457,16 @@ def pin_append_rope(O):
     want = np.zeros(8, np.float32)
     want[1], want[5] = np.float32(math.cos(100.0)), np.float32(math.sin(100.0))
     assert np.array_equal(c.k[0, 0, 5], want)
+    # queries: position 0 keeps every dtype's values; the golden vector turns
+    # like the key, then rounds to the query dtype
+    # (values compared through torch's bf16, so -0 and +0 count as equal)
+    q = w.k[:3].astype(np.float32)
+    bf = lambda y: torch.from_numpy(np.ascontiguousarray(y).view(np.int16)).view(torch.bfloat16).double().numpy()  # noqa: E731
+    for dt, conv, val in (("f32", lambda y: y, lambda y: y), ("f16", lambda y: y.astype(np.float16), lambda y: y),
+                          ("bf16", lambda y: torch.from_numpy(y).to(torch.bfloat16).double().numpy(), bf)):
+        assert np.array_equal(val(O.ref_rope_q(q, [0, 0, 0], 1e4, "interleaved", dt)), conv(q))
+        got = val(O.ref_rope_q(_unit(8, 1), [1000], 1e4, "half", dt))
+        assert np.array_equal(got[0, 0], conv(want))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -48,6 +48,8 @@ MUTANTS = [
     ("rope_rotates_v", "ref_append(cache, k_rot.astype(np.float32), v_new, slot_mapping)",
      "ref_append(cache, k_rot.astype(np.float32), rope_f64(np.asarray(v_new, dtype=np.float32), "
      "positions, theta, style).astype(np.float32), slot_mapping)"),
+    ("rope_q_left_unrotated", "return storage_from_f32(rot.astype(np.float32), dtype)",
+     "return storage_from_f32(np.asarray(q, dtype=np.float32), dtype)"),
     ("rope_f16_intermediate", "ref_append(cache, k_rot.astype(np.float32), v_new, slot_mapping)",
      "ref_append(cache, k_rot.astype(np.float16).astype(np.float32), v_new, slot_mapping)"),
 ]
