@@ -186,12 +186,15 @@ def rope_f64(x, positions, theta, style: str = "half") -> np.ndarray:
     implementations); "interleaved" pairs 2i with 2i + 1.
 
     x [T, H, d]; positions [T] integers; theta the base (taken at the fp32
-    value the library receives)."""
+    value the library receives).  The pair frequencies theta^(-2i/d) are held
+    as fp32 numbers (the power evaluated in float64, rounded once), the usual
+    storage of a RoPE frequency table; the angle, its cosine and sine and the
+    rotation are float64."""
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     h = d // 2
     i = np.arange(h, dtype=np.float64)
-    inv_freq = np.float64(np.float32(theta)) ** (-2.0 * i / d)
+    inv_freq = (np.float64(np.float32(theta)) ** (-2.0 * i / d)).astype(np.float32).astype(np.float64)
     ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
     c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
     if style == "half":

@@ -375,25 +375,29 @@ def _unit(d, i):
 
 
 def pin_rope_golden_angles(O):
-    """Hand-derived angles: with theta = 10^4 and d = 8 the four pairs turn at
-    1, 1/10, 1/100, 1/1000 rad per position, so position 1000 turns them by
-    1000, 100, 10 and 1 rad; with theta = 100 and d = 4 position 10 turns the
-    two pairs by 10 and 1 rad.  A unit vector on a pair's first coordinate
-    goes to (cos, sin) on (first, second); one on the second coordinate to
-    (-sin, cos) -- a rotation by +angle, as in the published definition."""
-    for d, theta, pos, angles in ((8, 1e4, 1000, (1000.0, 100.0, 10.0, 1.0)),
-                                  (4, 100.0, 10, (10.0, 1.0))):
+    """Hand-derived angles: with theta = 2^16 and d = 8 the four pairs turn at
+    1, 1/16, 1/256, 1/4096 rad per position (exact in fp32), so position 4096
+    turns them by 4096, 256, 16 and 1 rad; with theta = 256 and d = 4,
+    position 16 turns the two pairs by 16 and 1 rad.  With theta = 10^4 and
+    d = 8 the rates are 1, 1/10, 1/100, 1/1000 up to their fp32 rounding
+    (relative 2^-24), so position 1000 turns by 1000, 100, 10, 1 rad within
+    about 1e-5.  A unit vector on a pair's first coordinate goes to (cos, sin)
+    on (first, second); one on the second coordinate to (-sin, cos) -- a
+    rotation by +angle, as in the published definition."""
+    for d, theta, pos, angles, tol in ((8, 65536.0, 4096, (4096.0, 256.0, 16.0, 1.0), 1e-12),
+                                       (4, 256.0, 16, (16.0, 1.0), 1e-12),
+                                       (8, 1e4, 1000, (1000.0, 100.0, 10.0, 1.0), 1e-4)):
         for style in ("half", "interleaved"):
             for i, ang in enumerate(angles):
                 first, second = (i, i + d // 2) if style == "half" else (2 * i, 2 * i + 1)
                 want = np.zeros(d)
                 want[first], want[second] = math.cos(ang), math.sin(ang)
                 got = O.rope_f64(_unit(d, first), [pos], theta, style)[0, 0]
-                assert np.max(np.abs(got - want)) < 1e-9, (d, style, i)
+                assert np.max(np.abs(got - want)) < tol, (d, style, i)
                 want = np.zeros(d)
                 want[first], want[second] = -math.sin(ang), math.cos(ang)
                 got = O.rope_f64(_unit(d, second), [pos], theta, style)[0, 0]
-                assert np.max(np.abs(got - want)) < 1e-9, (d, style, i)
+                assert np.max(np.abs(got - want)) < tol, (d, style, i)
 
 
 def pin_rope_group_laws(O):
@@ -452,8 +456,8 @@ def pin_append_rope(O):
             assert np.array_equal(plain.v_scales, rot.v_scales)
         s0 = int(w.slot_mapping[0])
         assert np.array_equal(plain.k[s0 // PS, :, s0 % PS], rot.k[s0 // PS, :, s0 % PS])
-    c = O.PagedCache(1, 1, 8, "f32")
-    O.ref_append_rope(c, _unit(8, 1), np.zeros((1, 1, 8), np.float32), [5], [1000], 1e4, "half")
+    c = O.PagedCache(1, 1, 8, "f32")      # pair 1 turns at 1/16 rad per position: 100 rad
+    O.ref_append_rope(c, _unit(8, 1), np.zeros((1, 1, 8), np.float32), [5], [1600], 65536.0, "half")
     want = np.zeros(8, np.float32)
     want[1], want[5] = np.float32(math.cos(100.0)), np.float32(math.sin(100.0))
     assert np.array_equal(c.k[0, 0, 5], want)
@@ -465,7 +469,7 @@ def pin_append_rope(O):
     for dt, conv, val in (("f32", lambda y: y, lambda y: y), ("f16", lambda y: y.astype(np.float16), lambda y: y),
                           ("bf16", lambda y: torch.from_numpy(y).to(torch.bfloat16).double().numpy(), bf)):
         assert np.array_equal(val(O.ref_rope_q(q, [0, 0, 0], 1e4, "interleaved", dt)), conv(q))
-        got = val(O.ref_rope_q(_unit(8, 1), [1000], 1e4, "half", dt))
+        got = val(O.ref_rope_q(_unit(8, 1), [1600], 65536.0, "half", dt))
         assert np.array_equal(got[0, 0], conv(want))
 
 

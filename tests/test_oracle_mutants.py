@@ -50,6 +50,8 @@ MUTANTS = [
      "positions, theta, style).astype(np.float32), slot_mapping)"),
     ("rope_q_left_unrotated", "return storage_from_f32(rot.astype(np.float32), dtype)",
      "return storage_from_f32(np.asarray(q, dtype=np.float32), dtype)"),
+    ("rope_frequency_half_precision", ".astype(np.float32).astype(np.float64)\n    ang",
+     ".astype(np.float16).astype(np.float64)\n    ang"),
     ("rope_f16_intermediate", "ref_append(cache, k_rot.astype(np.float32), v_new, slot_mapping)",
      "ref_append(cache, k_rot.astype(np.float16).astype(np.float32), v_new, slot_mapping)"),
 ]
