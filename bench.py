@@ -43,6 +43,7 @@ DESC = {
     "C4": "chunked causal prefill, bf16 q/KV, Qwen2.5-1.5B shape: 8 x 512-token chunks over prefixes U[0,3584], 12 q / 2 KV heads, head_dim 128",
     "C5": "paged decode, int8 KV + per-token-head fp32 scales, TinyLlama-1.1B shape: batch 128, 32 q / 4 KV heads, head_dim 64, ctx 2048",
     "M1": "mixed batch in one call: the C2 decode batch (64 one-token chunks, ctx U[512,4096]) and the C4 chunks (8 x 512 tokens), 12 q / 2 KV heads, head_dim 128, bf16",
+    "R1": "append with RoPE on K and q (rotate-half, theta 1e6), the C4 chunks' 4096 new tokens, bf16 K/V/q in and bf16 cache, 12 q / 2 KV heads, head_dim 128",
     "M2": "decode-heavy mixed batch in one call: the C2 decode batch (64 one-token chunks, ctx U[512,4096]) and 4 chunks of 64 tokens over 1024-token prefixes, 12 q / 2 KV heads, head_dim 128, bf16",
 }
 
@@ -129,9 +130,11 @@ class Gpu:
         self.torch.cuda.synchronize()
 
     def timed_steps(self, step_fn, inner_fn, steps, warmup, flush=True):
-        """Run warmup + steps; each step is flushed (outside the events) and
-        bracketed by events; `inner_fn` is the dominant call, bracketed by its
-        own pair of events inside the step."""
+        """Run warmup, then two timed passes of `steps` steps each, every step
+        preceded by the flush (outside the events).  Pass one brackets whole
+        steps with events (nothing else recorded inside them); pass two
+        brackets only `inner_fn`, the dominant call, so the step time carries
+        no event of the inner timing."""
         torch = self.torch
         for _ in range(warmup):
             if flush:
@@ -144,12 +147,16 @@ class Gpu:
         for i in range(steps):
             if flush:
                 self.flush()
-            e0, e1, e2, e3 = ev[i]
-            e0.record()
-            step_fn(inner_fn, e1, e2)
-            e3.record()
+            ev[i][0].record()
+            step_fn(inner_fn)
+            ev[i][3].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        for i in range(steps):
+            if flush:
+                self.flush()
+            step_fn(inner_fn, ev[i][1], ev[i][2])
+        torch.cuda.synchronize()
         step_ms = [e[0].elapsed_time(e[3]) for e in ev]
         inner_ms = [e[1].elapsed_time(e[2]) for e in ev]
         return step_ms, inner_ms, wall
@@ -324,6 +331,53 @@ def bench_mixed(g: Gpu, name: str, steps: int, warmup: int):
     }
 
 
+def bench_rope(g: Gpu, steps: int, warmup: int):
+    """R1: the fused append with RoPE (K rotated and stored, V stored, q
+    rotated in place) against the plain append of the same K/V."""
+    from workloads import make_workload
+    torch = g.torch
+    w = make_workload("C4")
+    rows = w.new_token_rows()
+    T = len(rows)
+    k, v, _, _ = g.pool(w)
+    k_new = g.t(w.k[rows]).to(torch.bfloat16)
+    v_new = g.t(w.v[rows]).to(torch.bfloat16)
+    slots = g.t(w.slot_mapping[rows])
+    q = g.t(w.q).to(torch.bfloat16)
+    pos = torch.cat([torch.arange(int(c) - int(n), int(c), dtype=torch.int32)
+                     for c, n in zip(w.context_lens, w.q_lens)]).to(g.dev)
+    assert pos.numel() == T == q.shape[0]
+
+    def fused():
+        g.pkv.paged_kv_append_rope(k_new, v_new, slots, pos, k, v, 1e6, "half", q=q)
+
+    def plain():
+        g.pkv.paged_kv_append(k_new, v_new, slots, k, v)
+
+    def step(inner, e1=None, e2=None):
+        if e1 is not None:
+            e1.record()
+        inner()
+        if e2 is not None:
+            e2.record()
+
+    log(f"[bench] R1: {warmup} warmup + {steps} timed steps, fused RoPE append and plain append")
+    _, f_ms, _ = g.timed_steps(step, fused, steps, warmup)
+    _, p_ms, _ = g.timed_steps(step, plain, steps, warmup)
+    sf, sp = stats(f_ms), stats(p_ms)
+    hq, hkv, d = w.num_q_heads, w.num_kv_heads, w.head_dim
+    # read K, V, q, slots, positions; write K, V (bf16) and q
+    nbytes = T * (2 * (2 * hkv * d + hq * d) * 2 + 8 + 4)
+    gbs = nbytes / (sf["mean"] * 1e-3) / 1e9
+    return {
+        "workload": "R1", "desc": DESC["R1"], "tokens": T,
+        "fused_call_ms": sf, "plain_append_call_ms": sp,
+        "algorithmic_bytes": nbytes, "fused_gbs": gbs,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+    }
+
+
 def cpu_baseline(w, gpu_out, budget_s: float):
     """The oracle as it stands, timed on the host: one step = oracle append
     of the step's new tokens + oracle decode of the whole batch, repeated
@@ -372,13 +426,13 @@ def main():
                     help="seconds of oracle CPU work for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of workloads to run (C1..C5, M1, M2); default all")
+                    help="comma list of workloads to run (C1..C5, M1, M2, R1); default all")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2"}
+    only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2", "R1"}
 
     g = Gpu()
     extras = {}
@@ -399,6 +453,8 @@ def main():
     for name in ("M1", "M2"):
         if name in only:
             extras[f"mixed_{name}"] = bench_mixed(g, name, args.steps, args.warmup)
+    if "R1" in only:
+        extras["rope_append_R1"] = bench_rope(g, args.steps, args.warmup)
 
     line = {
         "metric": "decode KV GB/s (% HBM peak) + seq-tokens/s; prefill TFLOP/s (% MFMA)",

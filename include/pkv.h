@@ -109,6 +109,54 @@ int paged_kv_append(const void* k_new, const void* v_new, int new_dtype,
                     int cache_dtype, int num_pages, int num_kv_heads, int head_dim,
                     int page_size, pkv_stream_t stream);
 
+/* Pairing of coordinates for paged_kv_append_rope. */
+enum {
+  PKV_ROPE_HALF = 1,        /* coordinate i with i + head_dim/2 (Llama, Qwen2) */
+  PKV_ROPE_INTERLEAVED = 2  /* coordinate 2i with 2i + 1 */
+};
+
+/*
+ * paged_kv_append_rope - paged_kv_append with rotary position embedding on K
+ * (and optionally on the queries) in the same launch.
+ *
+ * RoPE with a configurable base theta in every forward path (TinyLoop
+ * "Current Status", table "Model architecture support", row "RoPE"), fused
+ * into the append so new K is read and written once.  Coordinate pair i of
+ * a head vector, 0 <= i < head_dim/2, is rotated by the angle
+ * positions[j] * rope_theta^(-2i/head_dim) (RoFormer's definition):
+ * (a, b) -> (a cos - b sin, b cos + a sin), a the pair's first coordinate.
+ * The pairing is rope_style (PKV_ROPE_HALF or PKV_ROPE_INTERLEAVED).
+ *
+ *   k_new, v_new, new_dtype, slot_mapping, num_tokens, k_cache, v_cache,
+ *   k_scales, v_scales, cache_dtype, num_pages, num_kv_heads, head_dim,
+ *   page_size      as for paged_kv_append; K is rotated, V is stored as
+ *                  paged_kv_append stores it.
+ *   positions      [num_tokens] int32 token positions (any value).
+ *   q              NULL, or [num_tokens][num_q_heads][head_dim] of q_dtype
+ *                  (F32/BF16/F16), rotated in place at the same positions,
+ *                  whatever the token's slot.  Must not overlap the other
+ *                  buffers.
+ *   rope_theta     the base, finite and > 0 (else PKV_ERR_INVALID_ARG).
+ *
+ * Arithmetic: each pair frequency rope_theta^(-2i/head_dim) is evaluated in
+ * double and rounded once to fp32 (the usual storage of a frequency table);
+ * the angle (position times that fp32 frequency), its cosine and sine and the
+ * rotation are evaluated in IEEE double (products and the sum rounded
+ * separately); the rotated value
+ * is rounded to fp32, then converted to the cache dtype (K) or the query
+ * dtype (q) exactly as paged_kv_append converts an fp32 input.  The double
+ * cosine and sine are those of the device math library, so a value lying
+ * within about 1e-16 relative of an fp32 rounding boundary may round either
+ * way: results agree with a correctly rounded evaluation to within one unit
+ * in the last place of the stored type (one int8 code).
+ */
+int paged_kv_append_rope(const void* k_new, const void* v_new, int new_dtype,
+                         const int64_t* slot_mapping, const int32_t* positions, int num_tokens,
+                         void* q, int q_dtype, int num_q_heads, float rope_theta, int rope_style,
+                         void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                         int cache_dtype, int num_pages, int num_kv_heads, int head_dim,
+                         int page_size, pkv_stream_t stream);
+
 /*
  * paged_attn_decode - one query token per sequence over its paged context.
  *

@@ -48,6 +48,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_kv_append.restype = _c_int
     lib.paged_kv_append.argtypes = [_vp, _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _vp]
+    lib.paged_kv_append_rope.restype = _c_int
+    lib.paged_kv_append_rope.argtypes = [_vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int, _c_int,
+                                         _c_float, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                                         _c_int, _c_int, _c_int, _vp]
     lib.paged_attn_decode.restype = _c_int
     lib.paged_attn_decode.argtypes = [_vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp,
                                       _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -124,6 +128,24 @@ def paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales=None,
         _ptr(k_new), _ptr(v_new), _code(k_new), _ptr(slot_mapping), int(slot_mapping.numel()),
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _code(k_cache),
         num_pages, hkv, d, page, _stream(stream)))
+
+
+ROPE_STYLES = {"half": 1, "interleaved": 2}
+
+
+def paged_kv_append_rope(k_new, v_new, slot_mapping, positions, k_cache, v_cache, rope_theta,
+                         rope_style="half", q=None, k_scales=None, v_scales=None,
+                         stream=None) -> None:
+    """paged_kv_append with RoPE on K; positions int32 [T]; q (optional)
+    [T, Hq, d] is rotated in place.  rope_style "half" or "interleaved"."""
+    _dev(k_new, v_new, slot_mapping, positions, k_cache, v_cache, k_scales, v_scales, q)
+    num_pages, hkv, page, d = k_cache.shape
+    hq = 0 if q is None else int(q.shape[1])
+    _check("paged_kv_append_rope", load_library().paged_kv_append_rope(
+        _ptr(k_new), _ptr(v_new), _code(k_new), _ptr(slot_mapping), _ptr(positions),
+        int(slot_mapping.numel()), _ptr(q), 0 if q is None else _code(q), hq, float(rope_theta),
+        ROPE_STYLES[rope_style], _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _code(k_cache), num_pages, hkv, d, page, _stream(stream)))
 
 
 def paged_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,

@@ -23,7 +23,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert set(names) == {
-        "pkv_abi_version", "pkv_status_string", "paged_kv_append", "paged_attn_decode",
+        "pkv_abi_version", "pkv_status_string", "paged_kv_append", "paged_kv_append_rope",
+        "paged_attn_decode",
         "paged_attn_decode_workspace_bytes", "paged_attn_prefill_chunk",
         "paged_attn_prefill_workspace_bytes", "paged_attn_mixed", "paged_attn_mixed_workspace_bytes"}
     for n in names:
@@ -162,3 +163,29 @@ def test_append_rejects(lib, over, code):
 
 def test_append_zero_tokens_is_noop(lib):
     assert _append(lib, T=0, k=None, v=None, slots=None) == 0
+
+
+def _append_rope(lib, **over):
+    a = dict(k=FAKE, v=FAKE, nd=0, slots=FAKE, pos=FAKE, T=4, q=None, qd=0, hq=0, theta=1e4,
+             style=1, kc=FAKE, vc=FAKE, ks=None, vs=None, cd=1, np_=32, hkv=2, d=64, ps=16, st=None)
+    a.update(over)
+    return lib.paged_kv_append_rope(*a.values())
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    ({"T": -1}, INVALID), ({"nd": 3}, INVALID), ({"cd": 5}, INVALID), ({"cd": 3}, INVALID),
+    ({"np_": 0}, INVALID), ({"ps": 8}, UNSUPPORTED), ({"d": 32}, UNSUPPORTED),
+    ({"slots": None}, INVALID), ({"pos": None}, INVALID), ({"style": 0}, INVALID),
+    ({"style": 3}, INVALID), ({"theta": 0.0}, INVALID), ({"theta": -1.0}, INVALID),
+    ({"theta": float("inf")}, INVALID), ({"theta": float("nan")}, INVALID),
+    ({"q": FAKE, "hq": 0, "qd": 0}, INVALID), ({"q": FAKE, "hq": 4, "qd": 3}, INVALID),
+    ({"kc": FAKE + 4}, MISALIGNED), ({"slots": FAKE + 4}, MISALIGNED),
+    ({"pos": FAKE + 2}, MISALIGNED), ({"q": FAKE + 8, "hq": 4}, MISALIGNED),
+])
+def test_append_rope_rejects(lib, over, code):
+    assert _append_rope(lib, **over) == code
+
+
+def test_append_rope_zero_tokens_is_noop(lib):
+    assert _append_rope(lib, T=0, k=None, v=None, slots=None, pos=None) == 0

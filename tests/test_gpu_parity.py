@@ -76,6 +76,26 @@ def test_append_bit_exact(pkv, cache_dtype, new_dtype, d):
         assert np.array_equal(gvs.cpu().numpy().view(np.uint32), host.v_scales.view(np.uint32))
 
 
+def test_append_full_size_bf16_and_out_of_pool_slots(pkv):
+    """Every token of the bf16 decode workload (Qwen2.5-1.5B heads, ~150k
+    tokens over a scattered 20k-page pool) appended from fp32 in one call and
+    compared byte for byte; tokens whose slot lies past the pool are skipped."""
+    w, _ = config_case("C2")
+    say("append C2 full size bf16")
+    slots = w.slot_mapping.copy()
+    beyond = [7, 1000, len(slots) - 1]
+    slots[beyond] = w.num_pages * 16 + np.array([0, 5, 10**9])
+    host = oracle.PagedCache(w.num_pages, w.num_kv_heads, w.head_dim, "bf16")
+    gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
+    pkv.paged_kv_append(torch.from_numpy(w.k).cuda(), torch.from_numpy(w.v).cuda(),
+                        torch.from_numpy(slots).cuda(), gk, gv)
+    torch.cuda.synchronize()
+    slots[beyond] = -1                      # the oracle's way of skipping a token
+    oracle.ref_append(host, w.k, w.v, slots)
+    assert np.array_equal(gpu_to_np_bits(gk), host.k)
+    assert np.array_equal(gpu_to_np_bits(gv), host.v)
+
+
 def test_append_full_size_int8(pkv):
     w, _ = config_case("C5")
     say("append C5 full size int8")

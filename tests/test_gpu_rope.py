@@ -1,0 +1,174 @@
+"""GPU parity of the append with RoPE (paged_kv_append_rope) against the
+oracle's ref_append_rope / ref_rope_q.
+
+The rotation is evaluated in fp64 on both sides and rounded once to fp32;
+the device's double cosine and sine may differ from the host's by an ulp of
+fp64, which moves the fp32 rounding only for a value within about 1e-16 of
+a rounding boundary.  So the bar is: V, tokens at position 0 and untouched
+slots byte for byte; every rotated value within one unit in the last place
+of its stored type (one int8 code); and at most a handful of values not
+bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TORCH_DT, gpu_to_np_bits, np_to_gpu, say
+from workloads import custom_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_attention_10_amd as lib
+    return lib
+
+
+def _ordered(bits: np.ndarray) -> np.ndarray:
+    """Float bit patterns -> integers in the order of the values (+0 == -0)."""
+    if bits.dtype.itemsize == 4:
+        a = bits.view(np.int32).astype(np.int64)
+        return np.where(a < 0, -(2**31) - a, a)
+    a = bits.view(np.int16).astype(np.int64)
+    return np.where(a < 0, -(2**15) - a, a)
+
+
+def _close(got: np.ndarray, want: np.ndarray, kind: str, what: str):
+    """Within one ulp (one code for int8); returns the count not identical."""
+    if kind == "i8":
+        d = np.abs(got.astype(np.int64) - want.astype(np.int64))
+    else:
+        d = np.abs(_ordered(np.ascontiguousarray(got)) - _ordered(np.ascontiguousarray(want)))
+    if d.max(initial=0) > 1:
+        at = np.unravel_index(int(np.argmax(d)), d.shape)
+        say(f"{what}: worst at {at}: got {got[at]!r} want {want[at]!r}")
+    assert d.max(initial=0) <= 1, f"{what}: {int(d.max())} ulp"
+    return int(np.count_nonzero(d))
+
+
+def _case(T, hkv, hq, d, seed):
+    w = custom_workload(context_lens=[T], num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                        kv_dtype="f32", num_pages=(T + 15) // 16 + 4, seed=seed)
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(0, 1 << 18, size=T).astype(np.int32)
+    pos[:4] = [0, 1, 2**31 - 1, -5]
+    q = rng.standard_normal((T, hq, d)).astype(np.float32)
+    return w, pos, q
+
+
+@pytest.mark.parametrize("cache_dtype", ["f32", "bf16", "f16", "i8"])
+@pytest.mark.parametrize("new_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16"), ("f16", "f32"),
+                                               ("f32", "f16")])
+@pytest.mark.parametrize("d,style", [(64, "half"), (128, "half"), (64, "interleaved"),
+                                     (128, "interleaved")])
+def test_append_rope_matches_oracle(pkv, cache_dtype, new_dtype, q_dtype, d, style):
+    say(f"append_rope cache={cache_dtype} new={new_dtype} q={q_dtype} d={d} {style}")
+    T, hkv, hq = 211, 2, 6
+    w, pos, qh = _case(T, hkv, hq, d, seed=500 + d)
+    k, v = w.k.copy(), w.v.copy()
+    k[5, 0, :6] = [0.0, -0.0, 1e-40, -3e-39, 2.0**-25, 1.00390625]     # zeros, subnormals, a bf16 tie
+    v[6, 1, :] = 0.0
+    theta = 10000.0 if d == 128 else 500000.0
+    kt = torch.from_numpy(k).cuda().to(TORCH_DT[new_dtype])
+    vt = torch.from_numpy(v).cuda().to(TORCH_DT[new_dtype])
+    qt = torch.from_numpy(qh).cuda().to(TORCH_DT[q_dtype])
+    q_before = qt.float().cpu().numpy()
+    slots = w.slot_mapping.copy()
+    slots[[7, 100]] = -1
+    host = oracle.PagedCache(w.num_pages, hkv, d, cache_dtype)
+    for arr in (host.k, host.v) + ((host.k_scales, host.v_scales) if cache_dtype == "i8" else ()):
+        arr.view(np.uint8)[:] = 0xA5
+    gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
+    gks = np_to_gpu(host.k_scales) if cache_dtype == "i8" else None
+    gvs = np_to_gpu(host.v_scales) if cache_dtype == "i8" else None
+    pkv.paged_kv_append_rope(kt, vt, torch.from_numpy(slots).cuda(), torch.from_numpy(pos).cuda(),
+                             gk, gv, theta, style, q=qt, k_scales=gks, v_scales=gvs)
+    torch.cuda.synchronize()
+    oracle.ref_append_rope(host, kt.float().cpu().numpy(), vt.float().cpu().numpy(), slots, pos,
+                           theta, style)
+    # V and every slot the call does not own: byte for byte
+    assert np.array_equal(gpu_to_np_bits(gv).view(np.uint8), host.v.view(np.uint8))
+    got_k = gpu_to_np_bits(gk)
+    owned = np.zeros(host.k.shape[0] * 16, dtype=bool)
+    owned[slots[slots >= 0]] = True
+    owned = owned.reshape(-1, 16)
+    free = ~owned[:, None, :, None].repeat(hkv, 1).repeat(d, 3)
+    assert np.array_equal(got_k.view(np.uint8).reshape(got_k.shape + (-1,))[free],
+                          host.k.view(np.uint8).reshape(host.k.shape + (-1,))[free])
+    # position 0: K stored exactly as the oracle stores it
+    s0 = int(slots[0])
+    assert np.array_equal(got_k[s0 // 16, :, s0 % 16].view(np.uint8),
+                          host.k[s0 // 16, :, s0 % 16].view(np.uint8))
+    n_off = _close(got_k, host.k, cache_dtype, "K")
+    if cache_dtype == "i8":
+        assert np.array_equal(gvs.cpu().numpy().view(np.uint32), host.v_scales.view(np.uint32))
+        n_off += _close(gks.cpu().numpy(), host.k_scales, "f32", "K scales")
+    want_q = oracle.ref_rope_q(q_before, pos, theta, style, q_dtype)
+    got_q = gpu_to_np_bits(qt)
+    n_off += _close(got_q, want_q, q_dtype, "q")
+    say(f"  values off by one ulp: {n_off} of {got_k.size + got_q.size}")
+    assert n_off <= 8
+
+
+def test_rope_attention_end_to_end(pkv):
+    """Rotated queries and keys from one call, then decode over the cache:
+    matches the oracle's decode of the oracle's rotated cache and queries."""
+    say("append_rope + decode end to end")
+    d, hkv, hq, T = 128, 2, 8, 700
+    w, pos, _ = _case(T, hkv, hq, d, seed=520)
+    pos = np.arange(T, dtype=np.int32)                 # one sequence, positions 0..T-1
+    rng = np.random.default_rng(521)
+    q1 = rng.standard_normal((1, hq, d)).astype(np.float32)
+    host = oracle.PagedCache(w.num_pages, hkv, d, "bf16")
+    gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
+    kt = torch.from_numpy(w.k).cuda().to(torch.bfloat16)
+    vt = torch.from_numpy(w.v).cuda().to(torch.bfloat16)
+    qt = torch.from_numpy(q1).cuda()
+    # the query is the last token's: rotate it alone at position T-1
+    pkv.paged_kv_append_rope(kt, vt, torch.from_numpy(w.slot_mapping).cuda(),
+                             torch.from_numpy(pos).cuda(), gk, gv, 1e4, "half")
+    qpos = torch.tensor([T - 1], dtype=torch.int32, device="cuda")
+    scratch_k = torch.zeros((1, hkv, d), dtype=torch.bfloat16, device="cuda")
+    pkv.paged_kv_append_rope(scratch_k, scratch_k, torch.tensor([-1], device="cuda"), qpos, gk, gv,
+                             1e4, "half", q=qt)
+    out = pkv.paged_attn_decode(qt, gk, gv, torch.from_numpy(w.block_tables).cuda(),
+                                torch.from_numpy(w.context_lens).cuda(), T, w.scale)
+    torch.cuda.synchronize()
+    oracle.ref_append_rope(host, kt.float().cpu().numpy(), vt.float().cpu().numpy(), w.slot_mapping,
+                           pos, 1e4, "half")
+    rq = oracle.ref_rope_q(q1, [T - 1], 1e4, "half", "f32").astype(np.float64)
+    ref = oracle.ref_decode(rq, host, w.block_tables, w.context_lens, w.scale, hq)
+    assert oracle.max_abs_err(out.double().cpu().numpy(), ref) <= 1e-2
+
+
+def test_append_rope_full_size(pkv):
+    """The benchmarked launch: the 4096 new tokens of the chunked-prefill
+    workload (8 chunks of 512 over prefixes U[0, 3584]), 12 query / 2 KV
+    heads, head_dim 128, bf16 K/V/q, bf16 cache, theta 1e6, every value
+    checked against the oracle."""
+    from workloads import make_workload
+    say("append_rope full size (4096 chunk tokens)")
+    w = make_workload("C4")
+    rows = w.new_token_rows()
+    kt = torch.from_numpy(w.k[rows]).cuda().to(torch.bfloat16)
+    vt = torch.from_numpy(w.v[rows]).cuda().to(torch.bfloat16)
+    qt = torch.from_numpy(w.q).cuda().to(torch.bfloat16)
+    q_before = qt.float().cpu().numpy()
+    pos = np.concatenate([np.arange(int(c) - int(n), int(c)) for c, n in zip(w.context_lens, w.q_lens)])
+    pos = pos.astype(np.int32)
+    slots = w.slot_mapping[rows]
+    host = oracle.PagedCache(w.num_pages, w.num_kv_heads, w.head_dim, "bf16")
+    gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
+    pkv.paged_kv_append_rope(kt, vt, torch.from_numpy(slots).cuda(), torch.from_numpy(pos).cuda(),
+                             gk, gv, 1e6, "half", q=qt)
+    torch.cuda.synchronize()
+    oracle.ref_append_rope(host, kt.float().cpu().numpy(), vt.float().cpu().numpy(), slots, pos,
+                           1e6, "half")
+    assert np.array_equal(gpu_to_np_bits(gv), host.v)
+    n_off = _close(gpu_to_np_bits(gk), host.k, "bf16", "K")
+    n_off += _close(gpu_to_np_bits(qt), oracle.ref_rope_q(q_before, pos, 1e6, "half", "bf16"), "bf16", "q")
+    say(f"  values off by one ulp: {n_off}")
+    assert n_off <= 8
