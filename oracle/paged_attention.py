@@ -231,9 +231,11 @@ def ref_rope_q(q, positions, theta, style: str, dtype: str) -> np.ndarray:
     return storage_from_f32(rot.astype(np.float32), dtype)
 
 
-def gather_sequence(cache: PagedCache, block_row, n: int):
-    """Contiguous float64 K, V [n, Hkv, d] of one sequence's first n tokens."""
-    t = np.arange(n)
+def gather_sequence(cache: PagedCache, block_row, n: int, start: int = 0):
+    """Contiguous float64 K, V [n - start, Hkv, d] of the tokens at positions
+    [start, n) of one sequence (block-table entries of earlier pages are not
+    read)."""
+    t = np.arange(start, n)
     page = np.asarray(block_row, dtype=np.int64)[t // PAGE_SIZE]
     off = t % PAGE_SIZE
     ks = None if cache.k_scales is None else cache.k_scales[page, :, off][..., None]
@@ -251,8 +253,13 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
 
 
 def ref_decode(q, cache: PagedCache, block_tables, context_lens, scale,
-               num_q_heads: int) -> np.ndarray:
-    """Batched decode: out[b, h] = softmax(scale * K_b q_bh) V_b over [0, ctx_b).
+               num_q_heads: int, window: int = 0) -> np.ndarray:
+    """Batched decode: out[b, h] = softmax(scale * K_b q_bh) V_b over the
+    positions [lo_b, ctx_b): lo_b = 0, or with a sliding window of `window`
+    tokens (TinyLoop "Current Status", table "KV cache modes", row
+    "Sliding-window cache") lo_b = max(0, ctx_b - window), so the query at
+    position ctx_b - 1 sees its `window` most recent positions, itself
+    included.
 
     q: [B, Hq, d] (any float dtype, widened exactly).  Returns float64."""
     q = np.asarray(q, dtype=np.float64)
@@ -264,7 +271,8 @@ def ref_decode(q, cache: PagedCache, block_tables, context_lens, scale,
         n = int(context_lens[b])
         if n == 0:
             continue
-        K, V = gather_sequence(cache, block_tables[b], n)
+        lo = max(0, n - window) if window > 0 else 0
+        K, V = gather_sequence(cache, block_tables[b], n, lo)
         for h in range(Hq):
             g = h // G
             s = sc * (K[:, g, :] @ q[b, h])
@@ -274,10 +282,11 @@ def ref_decode(q, cache: PagedCache, block_tables, context_lens, scale,
 
 
 def ref_prefill_chunk(q, cache: PagedCache, block_tables, context_lens, cu_q_lens,
-                      scale) -> np.ndarray:
+                      scale, window: int = 0) -> np.ndarray:
     """Chunked causal prefill.  q: [T, Hq, d]; sequence b's chunk is rows
     cu_q_lens[b]:cu_q_lens[b+1]; row i of it attends to [0, P_b + i] with
-    P_b = context_lens[b] - C_b.  Returns float64 [T, Hq, d]."""
+    P_b = context_lens[b] - C_b, or with a sliding window of `window` tokens
+    to (P_b + i - window, P_b + i].  Returns float64 [T, Hq, d]."""
     q = np.asarray(q, dtype=np.float64)
     T, Hq, d = q.shape
     G = Hq // cache.num_kv_heads
@@ -291,13 +300,16 @@ def ref_prefill_chunk(q, cache: PagedCache, block_tables, context_lens, cu_q_len
         P = n - C
         if P < 0:
             raise ValueError("context shorter than its query chunk")
-        K, V = gather_sequence(cache, block_tables[b], n)
-        keypos = np.arange(n)[None, :]
+        lo = max(0, P - window + 1) if window > 0 else 0
+        K, V = gather_sequence(cache, block_tables[b], n, lo)
+        keypos = np.arange(lo, n)[None, :]
         rowpos = P + np.arange(C)[:, None]
         for h in range(Hq):
             g = h // G
             s = sc * (q[r0:r1, h, :] @ K[:, g, :].T)
             s = np.where(keypos <= rowpos, s, -np.inf)
+            if window > 0:
+                s = np.where(keypos > rowpos - window, s, -np.inf)
             out[r0:r1, h] = _softmax_rows(s) @ V[:, g, :]
     return out
 

@@ -473,4 +473,78 @@ def pin_append_rope(O):
         assert np.array_equal(got[0, 0], conv(want))
 
 
+# ------------------------------------------------------------------ sliding window
+def pin_window_bruteforce(O):
+    """Sliding window of W tokens: the query at position p attends exactly
+    the positions (p - W, p], checked with math.fsum brute force for decode
+    and for every chunk row (rows near the chunk start see keys of the
+    prefix, rows further on only keys of the chunk)."""
+    w = custom_workload(kind="prefill", context_lens=[40, 21, 18, 3], q_lens=[9, 21, 1, 3],
+                        num_q_heads=2, num_kv_heads=1, head_dim=4, num_pages=12, seed=81)
+    ks = [_seq(w, w.k, b) for b in range(w.batch)]
+    vs = [_seq(w, w.v, b) for b in range(w.batch)]
+    cache = write_paged_f32(O, ks, vs, w.block_tables, w.num_pages, 1, 4)
+    for W in (1, 5, 16, 17):
+        out = O.ref_prefill_chunk(w.q, cache, w.block_tables, w.context_lens, w.cu_q_lens, w.scale,
+                                  window=W)
+        for b in range(w.batch):
+            n, C = int(w.context_lens[b]), int(w.q_lens[b])
+            P = n - C
+            for i in range(C):
+                p = P + i
+                lo = max(0, p - W + 1)
+                row = int(w.cu_q_lens[b]) + i
+                for h in range(2):
+                    ref = brute_attention_row(w.q[row, h], ks[b][lo:p + 1], vs[b][lo:p + 1], 0, w.scale)
+                    assert np.max(np.abs(out[row, h] - ref)) <= 1e-12, (W, b, i, h)
+        qd = np.stack([w.q[int(w.cu_q_lens[b + 1]) - 1] for b in range(w.batch)])
+        dec = O.ref_decode(qd, cache, w.block_tables, w.context_lens, w.scale, 2, window=W)
+        for b in range(w.batch):
+            n = int(w.context_lens[b])
+            lo = max(0, n - W)
+            for h in range(2):
+                ref = brute_attention_row(qd[b, h], ks[b][lo:n], vs[b][lo:n], 0, w.scale)
+                assert np.max(np.abs(dec[b, h] - ref)) <= 1e-12, (W, b, h)
+
+
+def pin_window_special_cases(O):
+    """A window covering the whole context is full attention (bit for bit);
+    a window of one token returns the query's own V; block-table entries of
+    pages wholly before the window are never read (they hold ids far outside
+    the pool here)."""
+    w = custom_workload(kind="prefill", context_lens=[70, 33, 16], q_lens=[20, 33, 1],
+                        num_q_heads=4, num_kv_heads=2, head_dim=8, kv_dtype="bf16",
+                        num_pages=20, seed=82)
+    c = _filled_cache(O, w)
+    args = (w.block_tables, w.context_lens, w.cu_q_lens, w.scale)
+    full = O.ref_prefill_chunk(w.q, c, *args)
+    assert np.array_equal(O.ref_prefill_chunk(w.q, c, *args, window=70), full)
+    qd = np.stack([w.q[int(w.cu_q_lens[b + 1]) - 1] for b in range(w.batch)])
+    dfull = O.ref_decode(qd, c, w.block_tables, w.context_lens, w.scale, 4)
+    assert np.array_equal(O.ref_decode(qd, c, w.block_tables, w.context_lens, w.scale, 4, window=10**6), dfull)
+    one = O.ref_prefill_chunk(w.q, c, *args, window=1)
+    for b in range(w.batch):
+        n, C = int(w.context_lens[b]), int(w.q_lens[b])
+        for i in range(C):
+            p = n - C + i
+            page, off = int(w.block_tables[b][p // PS]), p % PS
+            v = O.bf16_bits_to_f64(c.v[page, :, :, off])            # [Hkv, d]
+            row = int(w.cu_q_lens[b]) + i
+            for h in range(4):
+                assert np.max(np.abs(one[row, h] - v[h // 2])) <= 1e-15
+    # evicted pages: ids outside the pool before the window's first page
+    bt = w.block_tables.copy()
+    W = 20
+    for b in range(w.batch):
+        n, C = int(w.context_lens[b]), int(w.q_lens[b])
+        first_page = max(0, n - C - W + 1) // PS
+        bt[b, :first_page] = 10**7
+    got = O.ref_prefill_chunk(w.q, c, bt, w.context_lens, w.cu_q_lens, w.scale, window=W)
+    assert np.array_equal(got, O.ref_prefill_chunk(w.q, c, *args, window=W))
+    for b in range(w.batch):
+        bt[b, :max(0, int(w.context_lens[b]) - W) // PS] = 10**7
+    got = O.ref_decode(qd, c, bt, w.context_lens, w.scale, 4, window=W)
+    assert np.array_equal(got, O.ref_decode(qd, c, w.block_tables, w.context_lens, w.scale, 4, window=W))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -37,6 +37,16 @@ MUTANTS = [
     ("bf16_round_half_up", "(u + 0x7FFF + ((u >> 16) & 1)) >> 16", "(u + 0x8000) >> 16"),
     ("bf16_truncates", "(u + 0x7FFF + ((u >> 16) & 1)) >> 16", "u >> 16"),
     ("append_ignores_padding", "keep = slots >= 0", "keep = slots >= -1"),
+    ("window_decode_one_short", "lo = max(0, n - window) if window > 0 else 0",
+     "lo = max(0, n - window + 1) if window > 0 else 0"),
+    ("window_decode_one_long", "lo = max(0, n - window) if window > 0 else 0",
+     "lo = max(0, n - window - 1) if window > 0 else 0"),
+    ("window_prefill_mask_inclusive", "keypos > rowpos - window", "keypos >= rowpos - window"),
+    ("window_prefill_from_chunk_end", "keypos > rowpos - window", "keypos > P + C - 1 - window"),
+    ("window_prefill_mask_dropped", "            if window > 0:\n                s = np.where(",
+     "            if window < 0:\n                s = np.where("),
+    ("window_prefill_first_key_late", "lo = max(0, P - window + 1) if window > 0 else 0",
+     "lo = max(0, P - window + 2) if window > 0 else 0"),
     ("rope_turns_backwards", "ra = a * c - b * s\n    rb = b * c + a * s",
      "ra = a * c + b * s\n    rb = b * c - a * s"),
     ("rope_not_a_rotation", "rb = b * c + a * s", "rb = b * c - a * s"),
