@@ -30,6 +30,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -44,6 +46,7 @@ DESC = {
     "C5": "paged decode, int8 KV + per-token-head fp32 scales, TinyLlama-1.1B shape: batch 128, 32 q / 4 KV heads, head_dim 64, ctx 2048",
     "M1": "mixed batch in one call: the C2 decode batch (64 one-token chunks, ctx U[512,4096]) and the C4 chunks (8 x 512 tokens), 12 q / 2 KV heads, head_dim 128, bf16",
     "R1": "append with RoPE on K and q (rotate-half, theta 1e6), the C4 chunks' 4096 new tokens, bf16 K/V/q in and bf16 cache, 12 q / 2 KV heads, head_dim 128",
+    "W1": "sliding-window paged decode, bf16 KV, Qwen2.5-1.5B shape: batch 64, 12 q / 2 KV heads, head_dim 128, ctx U[16384,65536], window 4096, only the window's pages held (earlier block-table entries evicted)",
     "M2": "decode-heavy mixed batch in one call: the C2 decode batch (64 one-token chunks, ctx U[512,4096]) and 4 chunks of 64 tokens over 1024-token prefixes, 12 q / 2 KV heads, head_dim 128, bf16",
 }
 
@@ -53,7 +56,11 @@ def log(*a):
 
 
 def effective_kv_bytes(w) -> int:
-    tok = int(w.context_lens.astype(int).sum())
+    """K and V bytes the decode must read: every context token, or with a
+    sliding window the window's tokens."""
+    win = int(w.meta.get("window", 0))
+    ctx = w.context_lens.astype(np.int64)
+    tok = int((np.minimum(ctx, win) if win else ctx).sum())
     b = tok * w.num_kv_heads * w.head_dim * 2 * ELEM[w.kv_dtype]
     if w.kv_dtype == "i8":
         b += tok * w.num_kv_heads * 2 * 4
@@ -184,13 +191,14 @@ def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
     q = g.t(w.q)
     bt, cl = g.t(w.block_tables), g.t(w.context_lens)
     out = g.torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=g.torch.float32, device=g.dev)
+    window = int(w.meta.get("window", 0))
     nws = g.pkv.paged_attn_decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads,
-                                                  w.head_dim, w.max_context_len)
+                                                  w.head_dim, w.max_context_len, window)
     ws = g.torch.zeros(max(nws, 16), dtype=g.torch.uint8, device=g.dev)
 
     def decode():
         g.pkv.paged_attn_decode(q, k, v, bt, cl, w.max_context_len, w.scale, out=out,
-                                k_scales=ks, v_scales=vs, workspace=ws)
+                                k_scales=ks, v_scales=vs, workspace=ws, window=window)
 
     def step(inner, e1=None, e2=None):
         g.pkv.paged_kv_append(k_new, v_new, slots_new, k, v, ks, vs)
@@ -382,7 +390,6 @@ def cpu_baseline(w, gpu_out, budget_s: float):
     """The oracle as it stands, timed on the host: one step = oracle append
     of the step's new tokens + oracle decode of the whole batch, repeated
     until `budget_s` of CPU work; also the parity of the GPU output."""
-    import numpy as np
     from threadpoolctl import threadpool_info
     import oracle
     log("[bench] cpu baseline: oracle cache build (untimed)")
@@ -426,20 +433,21 @@ def main():
                     help="seconds of oracle CPU work for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of workloads to run (C1..C5, M1, M2, R1); default all")
+                    help="comma list of workloads to run (C1..C5, M1, M2, R1, W1); default all")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2", "R1"}
+    only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2", "R1",
+                                                        "W1"}
 
     g = Gpu()
     extras = {}
     head = None
     if "C2" in only:
         w2, head, out2 = bench_decode(g, "C2", args.steps, args.warmup)
-    for name in ("C3", "C5", "C1"):
+    for name in ("C3", "C5", "C1", "W1"):
         if name in only:
             _, r, _ = bench_decode(g, name, args.steps, args.warmup)
             r["roofline"] = {"bound": "hbm", "achieved": r["decode_call_gbs"], "peak": HBM_PEAK_GBS,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 #define PKV_PAGE_SIZE 16
 
 /* Element types.  PKV_BF16 is bfloat16 bits, PKV_I8 is int8 codes (KV only). */
@@ -163,8 +163,9 @@ int paged_kv_append_rope(const void* k_new, const void* v_new, int new_dtype,
  * Batched cached decode (TinyLoop "Current Status", table "Core inference",
  * row "Generation"; mini-llm README, true batched decode) over 16-token pages
  * with GQA.  context_lens[b] counts the query token itself, whose K/V must
- * already be appended; the query attends to positions [0, context_lens[b]).
- * A sequence with context_lens[b] == 0 gets zeros.
+ * already be appended; the query attends to positions [0, context_lens[b]),
+ * or with a sliding window to the `window` most recent of them.  A sequence
+ * with context_lens[b] == 0 gets zeros.
  *
  *   q              [batch][num_q_heads][head_dim], dtype q_dtype (F32/BF16/F16).
  *   k_cache, v_cache, k_scales, v_scales, kv_dtype   the pool (layout above);
@@ -176,6 +177,13 @@ int paged_kv_append_rope(const void* k_new, const void* v_new, int new_dtype,
  *                  max_blocks_per_seq*16; sizes the split of long contexts.
  *   num_pages      pool size in pages (page ids must be below it).
  *   scale          multiplies q.k before the softmax.
+ *   window         0 for the whole context, or a sliding window of `window`
+ *                  tokens (TinyLoop "Current Status", table "KV cache modes",
+ *                  row "Sliding-window cache"): the query at position
+ *                  p = context_lens[b] - 1 attends to positions (p - window, p].
+ *                  Block-table entries of pages wholly before the window are
+ *                  never read, so a cache that bounds its storage by the
+ *                  window may have recycled them.  Negative: PKV_ERR_INVALID_ARG.
  *   out            [batch][num_q_heads][head_dim], dtype out_dtype (F32/BF16/F16).
  *   workspace      device scratch of at least
  *                  paged_attn_decode_workspace_bytes(...) bytes (may be NULL
@@ -183,9 +191,10 @@ int paged_kv_append_rope(const void* k_new, const void* v_new, int new_dtype,
  *                  Calls that run concurrently must not share a workspace.
  *
  * Built for head_dim 64 and 128, page_size 16, any num_q_heads/num_kv_heads
- * ratio, max_context_len up to 262144 (PKV_ERR_UNSUPPORTED beyond).  Long
- * contexts are split into partitions whose softmax partials are merged with
- * their log-sum-exp weights by a second kernel on the same stream.
+ * ratio, keys spanning up to 262144 tokens (the whole context, or with a
+ * window the window; PKV_ERR_UNSUPPORTED beyond).  Long contexts are split
+ * into partitions whose softmax partials are merged with their log-sum-exp
+ * weights by a second kernel on the same stream.
  */
 int paged_attn_decode(const void* q, int q_dtype,
                       const void* k_cache, const void* v_cache,
@@ -193,7 +202,7 @@ int paged_attn_decode(const void* q, int q_dtype,
                       const int32_t* block_tables, int max_blocks_per_seq,
                       const int32_t* context_lens, int max_context_len,
                       int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                      int page_size, int num_pages, float scale,
+                      int page_size, int num_pages, float scale, int window,
                       void* out, int out_dtype,
                       void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
@@ -201,7 +210,7 @@ int paged_attn_decode(const void* q, int q_dtype,
  * contexts fit one partition, or for invalid shapes).  Pure host
  * arithmetic; touches no device. */
 size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
-                                         int head_dim, int max_context_len);
+                                         int head_dim, int max_context_len, int window);
 
 /*
  * paged_attn_prefill_chunk - a causal chunk of query tokens over its paged
@@ -213,7 +222,9 @@ size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_
  * chunk's own K/V must already be appended.  Sequence b's queries are rows
  * cu_q_lens[b] .. cu_q_lens[b+1]-1 of q; with C_b = cu_q_lens[b+1]-cu_q_lens[b]
  * and P_b = context_lens[b] - C_b (required >= 0), chunk row i sits at
- * absolute position P_b + i and attends to positions [0, P_b + i].
+ * absolute position P_b + i and attends to positions [0, P_b + i], or with
+ * window > 0 to (P_b + i - window, P_b + i]; block-table entries of pages
+ * wholly before the window of the chunk's first row are never read.
  *
  *   q              [num_tokens][num_q_heads][head_dim], dtype q_dtype.
  *   cu_q_lens      [batch+1] int32, cu_q_lens[0] == 0, non-decreasing,
@@ -236,13 +247,14 @@ int paged_attn_prefill_chunk(const void* q, int q_dtype,
                              const int32_t* context_lens, const int32_t* cu_q_lens,
                              int num_tokens, int max_q_len, int max_context_len,
                              int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                             int page_size, int num_pages, float scale,
+                             int page_size, int num_pages, float scale, int window,
                              void* out, int out_dtype,
                              void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
 /* Workspace bytes paged_attn_prefill_chunk needs (pure host arithmetic). */
 size_t paged_attn_prefill_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
-                                          int head_dim, int max_q_len, int max_context_len);
+                                          int head_dim, int max_q_len, int max_context_len,
+                                          int window);
 
 /*
  * paged_attn_mixed - prefill chunks and decode tokens of one batch in one call.
@@ -262,7 +274,8 @@ size_t paged_attn_prefill_workspace_bytes(int batch, int num_q_heads, int num_kv
  *                  contents on entry do not matter.
  *
  * Built for head_dim 64 and 128, page_size 16, kv_dtype PKV_BF16 or PKV_F16,
- * max_context_len up to 262144 (PKV_ERR_UNSUPPORTED otherwise).  A one-token
+ * decode keys spanning up to 262144 tokens (PKV_ERR_UNSUPPORTED otherwise);
+ * `window` as for paged_attn_prefill_chunk.  A one-token
  * chunk with context_lens[b] < 1 gets NaN, like any chunk longer than its
  * context.
  */
@@ -273,7 +286,7 @@ int paged_attn_mixed(const void* q, int q_dtype,
                      const int32_t* context_lens, const int32_t* cu_q_lens,
                      int num_tokens, int max_q_len, int max_context_len,
                      int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                     int page_size, int num_pages, float scale,
+                     int page_size, int num_pages, float scale, int window,
                      void* out, int out_dtype,
                      void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
@@ -282,7 +295,8 @@ int paged_attn_mixed(const void* q, int q_dtype,
  * paged_attn_decode when max_q_len < 128, and only as far as contexts beyond
  * 4096 tokens require otherwise.  Pure host arithmetic; touches no device. */
 size_t paged_attn_mixed_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
-                                        int head_dim, int max_q_len, int max_context_len);
+                                        int head_dim, int max_q_len, int max_context_len,
+                                        int window);
 
 #ifdef __cplusplus
 }

@@ -33,6 +33,9 @@ class PkvError(RuntimeError):
 _lib = None
 
 
+ABI_VERSION = 2   # PKV_ABI_VERSION of include/pkv.h this binding marshals for
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libpkv.so (once).  Raises if it has not been built."""
     global _lib
@@ -55,20 +58,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attn_decode.restype = _c_int
     lib.paged_attn_decode.argtypes = [_vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp,
                                       _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                      _c_float, _vp, _c_int, _vp, _c_size, _vp]
+                                      _c_float, _c_int, _vp, _c_int, _vp, _c_size, _vp]
     lib.paged_attn_decode_workspace_bytes.restype = _c_size
-    lib.paged_attn_decode_workspace_bytes.argtypes = [_c_int] * 5
+    lib.paged_attn_decode_workspace_bytes.argtypes = [_c_int] * 6
     lib.paged_attn_prefill_chunk.restype = _c_int
     lib.paged_attn_prefill_chunk.argtypes = [_vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int,
                                              _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                             _c_int, _c_int, _c_int, _c_int, _c_float, _vp,
-                                             _c_int, _vp, _c_size, _vp]
+                                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                             _vp, _c_int, _vp, _c_size, _vp]
     lib.paged_attn_prefill_workspace_bytes.restype = _c_size
-    lib.paged_attn_prefill_workspace_bytes.argtypes = [_c_int] * 6
+    lib.paged_attn_prefill_workspace_bytes.argtypes = [_c_int] * 7
     lib.paged_attn_mixed.restype = _c_int
     lib.paged_attn_mixed.argtypes = lib.paged_attn_prefill_chunk.argtypes
     lib.paged_attn_mixed_workspace_bytes.restype = _c_size
-    lib.paged_attn_mixed_workspace_bytes.argtypes = [_c_int] * 6
+    lib.paged_attn_mixed_workspace_bytes.argtypes = [_c_int] * 7
+    if lib.pkv_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {lib.pkv_abi_version()}, this binding needs "
+                          f"{ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -149,15 +155,15 @@ def paged_kv_append_rope(k_new, v_new, slot_mapping, positions, k_cache, v_cache
 
 
 def paged_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
-                                      max_context_len) -> int:
+                                      max_context_len, window=0) -> int:
     return int(load_library().paged_attn_decode_workspace_bytes(
-        batch, num_q_heads, num_kv_heads, head_dim, max_context_len))
+        batch, num_q_heads, num_kv_heads, head_dim, max_context_len, window))
 
 
 def paged_attn_prefill_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_q_len,
-                                       max_context_len) -> int:
+                                       max_context_len, window=0) -> int:
     return int(load_library().paged_attn_prefill_workspace_bytes(
-        batch, num_q_heads, num_kv_heads, head_dim, max_q_len, max_context_len))
+        batch, num_q_heads, num_kv_heads, head_dim, max_q_len, max_context_len, window))
 
 
 def _workspace(nbytes, workspace, device):
@@ -170,65 +176,65 @@ def _workspace(nbytes, workspace, device):
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                       out=None, out_dtype=torch.float32, k_scales=None, v_scales=None,
-                      workspace=None, stream=None):
+                      workspace=None, stream=None, window=0):
     """q [B, Hq, d] -> out [B, Hq, d].  block_tables int32 [B, W],
-    context_lens int32 [B] (each <= max_context_len)."""
+    context_lens int32 [B] (each <= max_context_len); window 0 = whole context."""
     B, hq, d = q.shape
     num_pages, hkv, page, _ = k_cache.shape
     if out is None:
         out = torch.empty((B, hq, d), dtype=out_dtype, device=q.device)
     _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales)
-    nbytes = paged_attn_decode_workspace_bytes(B, hq, hkv, d, max_context_len)
+    nbytes = paged_attn_decode_workspace_bytes(B, hq, hkv, d, max_context_len, window)
     workspace, wbytes = _workspace(nbytes, workspace, q.device)
     _check("paged_attn_decode", load_library().paged_attn_decode(
         _ptr(q), _code(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
         _code(k_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
-        int(max_context_len), B, hq, hkv, d, page, num_pages, float(scale), _ptr(out),
-        _code(out), _ptr(workspace), wbytes, _stream(stream)))
+        int(max_context_len), B, hq, hkv, d, page, num_pages, float(scale), int(window),
+        _ptr(out), _code(out), _ptr(workspace), wbytes, _stream(stream)))
     return out
 
 
 def paged_attn_mixed_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_q_len,
-                                     max_context_len) -> int:
+                                     max_context_len, window=0) -> int:
     return int(load_library().paged_attn_mixed_workspace_bytes(
-        batch, num_q_heads, num_kv_heads, head_dim, max_q_len, max_context_len))
+        batch, num_q_heads, num_kv_heads, head_dim, max_q_len, max_context_len, window))
 
 
 def paged_attn_mixed(q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, max_q_len,
                      max_context_len, scale, out=None, out_dtype=torch.float32, k_scales=None,
-                     v_scales=None, workspace=None, stream=None):
+                     v_scales=None, workspace=None, stream=None, window=0):
     """Same arguments and result as paged_attn_prefill_chunk; one-token chunks
     run as split decode partitions in the same launch."""
     return _varlen("paged_attn_mixed", paged_attn_mixed_workspace_bytes, q, k_cache, v_cache,
                    block_tables, context_lens, cu_q_lens, max_q_len, max_context_len, scale, out,
-                   out_dtype, k_scales, v_scales, workspace, stream)
+                   out_dtype, k_scales, v_scales, workspace, stream, window)
 
 
 def paged_attn_prefill_chunk(q, k_cache, v_cache, block_tables, context_lens, cu_q_lens,
                              max_q_len, max_context_len, scale, out=None,
                              out_dtype=torch.float32, k_scales=None, v_scales=None,
-                             workspace=None, stream=None):
+                             workspace=None, stream=None, window=0):
     """q [T, Hq, d] -> out [T, Hq, d]; cu_q_lens int32 [B+1]; context_lens
-    int32 [B] = prefix + chunk."""
+    int32 [B] = prefix + chunk; window 0 = the whole causal prefix."""
     return _varlen("paged_attn_prefill_chunk", paged_attn_prefill_workspace_bytes, q, k_cache,
                    v_cache, block_tables, context_lens, cu_q_lens, max_q_len, max_context_len,
-                   scale, out, out_dtype, k_scales, v_scales, workspace, stream)
+                   scale, out, out_dtype, k_scales, v_scales, workspace, stream, window)
 
 
 def _varlen(fn, ws_query, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, max_q_len,
-            max_context_len, scale, out, out_dtype, k_scales, v_scales, workspace, stream):
+            max_context_len, scale, out, out_dtype, k_scales, v_scales, workspace, stream, window):
     T, hq, d = q.shape
     B = int(context_lens.shape[0])
     num_pages, hkv, page, _ = k_cache.shape
     if out is None:
         out = torch.empty((T, hq, d), dtype=out_dtype, device=q.device)
     _dev(q, k_cache, v_cache, block_tables, context_lens, cu_q_lens, out, k_scales, v_scales)
-    nbytes = ws_query(B, hq, hkv, d, max_q_len, max_context_len)
+    nbytes = ws_query(B, hq, hkv, d, max_q_len, max_context_len, window)
     workspace, wbytes = _workspace(nbytes, workspace, q.device)
     _check(fn, getattr(load_library(), fn)(
         _ptr(q), _code(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
         _code(k_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
         _ptr(cu_q_lens), T, int(max_q_len), int(max_context_len), B, hq, hkv, d, page,
-        num_pages, float(scale), _ptr(out), _code(out), _ptr(workspace), wbytes,
+        num_pages, float(scale), int(window), _ptr(out), _code(out), _ptr(workspace), wbytes,
         _stream(stream)))
     return out

@@ -74,11 +74,12 @@ static void dispatch_kv(int kv, const DecodeArgs& a, pkv_stream_t stream) {
 using namespace pkv;
 
 extern "C" size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
-                                                    int head_dim, int max_context_len) {
+                                                    int head_dim, int max_context_len, int window) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
-      !head_dim_built(head_dim) || max_context_len < 0 || (long)max_context_len > kDecodeMaxContext)
+      !head_dim_built(head_dim) || max_context_len < 0 || window < 0 ||
+      !decode_span_supported(max_context_len, window))
     return 0;
-  DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+  DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, window);
   return decode_workspace_layout(batch, num_q_heads, head_dim, p).total;
 }
 
@@ -88,27 +89,28 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
                                  const int32_t* block_tables, int max_blocks_per_seq,
                                  const int32_t* context_lens, int max_context_len, int batch,
                                  int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                                 int num_pages, float scale, void* out, int out_dtype,
+                                 int num_pages, float scale, int window, void* out, int out_dtype,
                                  void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return PKV_ERR_INVALID_ARG;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
       num_pages <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE || batch > 65535)
+      (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE || batch > 65535 ||
+      window < 0)
     return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
     return PKV_ERR_INVALID_ARG;
   if ((kv_dtype == PKV_I8) != (k_scales != nullptr) || (kv_dtype == PKV_I8) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim) ||
-      (long)max_context_len > kDecodeMaxContext)
+      !decode_span_supported(max_context_len, window))
     return PKV_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(block_tables) || !aligned16(context_lens) ||
       (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)))
     return PKV_ERR_MISALIGNED;
 
-  DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+  DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, window);
   DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, head_dim, p);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (workspace && !aligned16(workspace)) return PKV_ERR_MISALIGNED;
@@ -138,6 +140,7 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
   a.num_pages = num_pages;
   a.tiles_per_split = p.tiles_per_split;
   a.nsplits = p.nsplits;
+  a.window = window;
   a.scale_log2 = scale * kLog2e;
 
   clear_launch_error();

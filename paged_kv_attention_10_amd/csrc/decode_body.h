@@ -28,8 +28,15 @@ struct DecodeArgs {
   int max_blocks, max_context_len;
   int batch, hq, hkv, group, head_tiles, num_pages;
   int tiles_per_split, nsplits;
+  int window;                 // sliding window in tokens, 0 = the whole context
   float scale_log2;
 };
+
+// First position a query at position ctx - 1 attends: ctx - window with a
+// sliding window, else 0.
+__device__ __forceinline__ int window_start(int ctx, int window) {
+  return window > 0 ? max(0, ctx - window) : 0;
+}
 
 constexpr float kDecodeLazyRescale = 8.0f;
 
@@ -154,14 +161,23 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   // ---- one round trip for the context length, the query and the page ids
   //      of the whole split (loaded before the context length says which of
   //      them the split uses and how its tiles divide over the waves; entries
-  //      past the context are never used)
+  //      past the context are never used).  With a sliding window the split's
+  //      pages follow from the window start, so the context length comes
+  //      first and entries of pages wholly before the window are not read.
   const int raw_ctx = a.context_lens[b];
+  bool bad = a.cu_q_lens && raw_ctx < 1;   // a chunk of one needs a context of at least one
   using SM = DecodeSmem<D>;
   int* const s_pid = reinterpret_cast<int*>(smem + SM::pid);
+  int lo = 0, t_lo = 0;                    // window start and its tile
+  if (a.window > 0) {
+    bool dummy = false;
+    lo = window_start(checked_ctx(raw_ctx, a.max_context_len, a.max_blocks, dummy), a.window);
+    t_lo = lo >> 5;
+  }
   {
-    const int sp0 = 2 * split * a.tiles_per_split;          // the split's first page
+    const int sp0 = 2 * (t_lo + split * a.tiles_per_split);   // the split's first page
     const int i = threadIdx.x;
-    if (i < 2 * a.tiles_per_split && sp0 + i < a.max_blocks)
+    if (i < 2 * a.tiles_per_split && sp0 + i < a.max_blocks && sp0 + i >= (lo >> 4))
       s_pid[i] = a.block_tables[(long)b * a.max_blocks + sp0 + i];
   }
 
@@ -196,14 +212,14 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
     }
   }
 
-  bool bad = a.cu_q_lens && raw_ctx < 1;   // a chunk of one needs a context of at least one
   const int ctx = checked_ctx(raw_ctx, a.max_context_len, a.max_blocks, bad);
   const int ntiles = (ctx + 31) >> 5;
-  const int nsplit_b = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  const int nsplit_b = (ntiles - t_lo + a.tiles_per_split - 1) / a.tiles_per_split;
   if (split >= (nsplit_b > 0 ? nsplit_b : 1)) return;
   const int npages = (ctx + kPage - 1) / kPage;
+  const int p_lo = lo >> 4;                                  // first page inside the window
   // the split's tiles, divided evenly over the waves in contiguous runs
-  const int st0 = split * a.tiles_per_split;
+  const int st0 = t_lo + split * a.tiles_per_split;
   const int stn = max(0, min(ntiles - st0, a.tiles_per_split));
   const int per = (stn + kDecodeWaves - 1) / kDecodeWaves;   // <= 32
   const int wt0 = st0 + wave * per;                          // first tile of the wave
@@ -213,7 +229,9 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   __syncthreads();   // the split's page ids are in LDS
   int pid = 0;
   if (lane < npw) {
-    pid = s_pid[wp0 - 2 * st0 + lane];
+    // a page wholly before the window (the first tile's first page at most)
+    // takes the window's first page instead; its keys are masked
+    pid = s_pid[max(wp0 + lane, p_lo) - 2 * st0];
     if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
   }
 
@@ -265,10 +283,10 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
     }
 
     // ---- scores of head c for tile tokens 8j + e, e = 4u + i; only the
-    //      tile holding the context end needs masking
+    //      tiles holding the context end or the window start need masking
     const int t = wt0 + li;
     const int tok0 = 32 * t + 8 * j;
-    const bool partial = (32 * t + 32 > ctx);
+    const bool partial = (32 * t + 32 > ctx) || (32 * t < lo);
     float sc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -279,7 +297,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
     if (partial) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (tok0 + e >= ctx) sc[e] = -INFINITY;
+        if (tok0 + e >= ctx || tok0 + e < lo) sc[e] = -INFINITY;
     }
     float mt = sc[0];
 #pragma unroll
@@ -312,7 +330,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float v = __uint_as_float(cur.v[blk][e >> 2][e & 3]);
-          if (partial && tok0 + e >= ctx) v = 0.f;
+          if (partial && (tok0 + e >= ctx || tok0 + e < lo)) v = 0.f;
           acc[blk] = mfma16x16x4(v, p[e], acc[blk]);
         }
       }
@@ -321,15 +339,16 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float x = p[e];
-        if constexpr (kI8) x = (tok0 + e < ctx) ? x * cur.vs[e >> 2][e & 3] : 0.f;
+        if constexpr (kI8) x = (tok0 + e < ctx && tok0 + e >= lo) ? x * cur.vs[e >> 2][e & 3] : 0.f;
         pv[e] = x;
       }
-      // V of tokens at or past the context end may hold anything: zero them
+      // V of tokens at or past the context end or before the window may
+      // hold anything: zero them
       u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
       if (partial) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (tok0 + e >= ctx) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          if (tok0 + e >= ctx || tok0 + e < lo) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
       }
       H8 phi, plo;
       if constexpr (kBF16) {
@@ -456,7 +475,8 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
   bool bad = a.cu_q_lens && raw_ctx < 1;
   const int ctx = checked_ctx(raw_ctx, a.max_context_len, a.max_blocks, bad);
   const int ntiles = (ctx + 31) >> 5;
-  const int ns = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  const int t_lo = window_start(ctx, a.window) >> 5;
+  const int ns = (ntiles - t_lo + a.tiles_per_split - 1) / a.tiles_per_split;
   if (ns <= 1) return;
   const float mine = lane < ns ? lse_l : -INFINITY;
   float M = mine;

@@ -73,10 +73,10 @@ static void dispatch_mixed(int kv, const DecodeArgs& da, const PrefillArgs& pa, 
 // dominate and are planned as a decode call.
 constexpr int kMixedLongChunk = 128;
 static DecodePlan mixed_plan(int batch, int num_q_heads, int num_kv_heads, int max_q_len,
-                             int max_context_len) {
+                             int max_context_len, int window) {
   return max_q_len >= kMixedLongChunk
-             ? plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, 0)
-             : plan_decode(batch, num_q_heads, num_kv_heads, max_context_len);
+             ? plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, window, 0)
+             : plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, window);
 }
 
 }  // namespace pkv
@@ -84,14 +84,15 @@ static DecodePlan mixed_plan(int batch, int num_q_heads, int num_kv_heads, int m
 using namespace pkv;
 
 extern "C" size_t paged_attn_mixed_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
-                                                   int head_dim, int max_q_len, int max_context_len) {
+                                                   int head_dim, int max_q_len, int max_context_len,
+                                                   int window) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
-      !head_dim_built(head_dim) || max_q_len < 0 || max_context_len < 0 ||
-      (long)max_context_len > kDecodeMaxContext)
+      !head_dim_built(head_dim) || max_q_len < 0 || max_context_len < 0 || window < 0 ||
+      !decode_span_supported(max_context_len, window))
     return 0;
   return decode_workspace_layout(batch, num_q_heads, head_dim,
                                  mixed_plan(batch, num_q_heads, num_kv_heads, max_q_len,
-                                            max_context_len)).total;
+                                            max_context_len, window)).total;
 }
 
 extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
@@ -100,14 +101,14 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
                                 const int32_t* context_lens, const int32_t* cu_q_lens,
                                 int num_tokens, int max_q_len, int max_context_len, int batch,
                                 int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                                int num_pages, float scale, void* out, int out_dtype,
+                                int num_pages, float scale, int window, void* out, int out_dtype,
                                 void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
   if (!k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens ||
       ((!q || !out) && num_tokens > 0))
     return PKV_ERR_INVALID_ARG;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
       num_pages <= 0 || max_blocks_per_seq <= 0 || num_tokens < 0 || max_q_len < 0 ||
-      max_context_len < 0 || max_q_len > max_context_len || batch > 65535 ||
+      max_context_len < 0 || max_q_len > max_context_len || batch > 65535 || window < 0 ||
       (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE)
     return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
@@ -115,7 +116,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   if ((kv_dtype == PKV_I8) != (k_scales != nullptr) || (kv_dtype == PKV_I8) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim) ||
-      (long)max_context_len > kDecodeMaxContext)
+      !decode_span_supported(max_context_len, window))
     return PKV_ERR_UNSUPPORTED;
   if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16) return PKV_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
@@ -123,7 +124,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
     return PKV_ERR_MISALIGNED;
   if (num_tokens == 0 || max_q_len == 0) return PKV_OK;
 
-  const DecodePlan p = mixed_plan(batch, num_q_heads, num_kv_heads, max_q_len, max_context_len);
+  const DecodePlan p = mixed_plan(batch, num_q_heads, num_kv_heads, max_q_len, max_context_len, window);
   const DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, head_dim, p);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (workspace && !aligned16(workspace)) return PKV_ERR_MISALIGNED;
@@ -153,6 +154,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   da.num_pages = num_pages;
   da.tiles_per_split = p.tiles_per_split;
   da.nsplits = p.nsplits;
+  da.window = window;
   da.scale_log2 = scale * kLog2e;
 
   PrefillArgs pa;
@@ -176,6 +178,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   pa.nrowblocks = ceil_div((long)max_q_len * pa.group, kPrefillRowsPerBlock);
   pa.scale_log2 = scale * kLog2e;
   pa.skip_single = 1;
+  pa.window = window;
   if (pa.nrowblocks > 65535) return PKV_ERR_INVALID_ARG;
 
   // no row block can hold work when every chunk has at most one token

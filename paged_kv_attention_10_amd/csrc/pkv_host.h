@@ -49,15 +49,32 @@ constexpr long kDecodeMaxContext = (long)kDecodeMaxSplits * kDecodeMaxTilesPerSp
 #endif
 constexpr long kDecodeTargetWorkgroups = PKV_DECODE_TARGET_WORKGROUPS;
 
+// Tiles a sequence's keys span at most: its whole context, or with a
+// sliding window of `window` tokens the window, which may start anywhere in
+// a tile.
+inline int decode_tiles(int max_context_len, int window) {
+  int t = max_context_len > 0 ? ceil_div(max_context_len, kDecodeTileTokens) : 1;
+  if (window > 0) {
+    const int tw = (window - 1) / kDecodeTileTokens + 2;
+    if (tw < t) t = tw;
+  }
+  return t;
+}
+
+// Whether the split plan covers that span (at most kDecodeMaxContext tokens).
+inline bool decode_span_supported(int max_context_len, int window) {
+  return (long)decode_tiles(max_context_len, window) * kDecodeTileTokens <= kDecodeMaxContext;
+}
+
 // target_workgroups = 0 asks for the fewest splits the context allows (a
 // mixed batch, where the prefill row blocks set the critical path and a
 // decode split would only add the merge).
 inline DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len,
-                              long target_workgroups = kDecodeTargetWorkgroups) {
+                              int window, long target_workgroups = kDecodeTargetWorkgroups) {
   DecodePlan p;
   int group = num_q_heads / num_kv_heads;
   p.head_tiles = ceil_div(group, 16);
-  int tiles_max = max_context_len > 0 ? ceil_div(max_context_len, kDecodeTileTokens) : 1;
+  int tiles_max = decode_tiles(max_context_len, window);
   long units = (long)batch * num_kv_heads * p.head_tiles;
   long want = (target_workgroups + units - 1) / units;
   if (want < 1) want = 1;
@@ -66,7 +83,7 @@ inline DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int 
   if (tps < kDecodeWaves) tps = kDecodeWaves;
   if (tps > kDecodeMaxTilesPerSplit) tps = kDecodeMaxTilesPerSplit;
   p.tiles_per_split = tps;
-  p.nsplits = ceil_div(tiles_max, tps);   // <= kDecodeMaxSplits for contexts <= kDecodeMaxContext
+  p.nsplits = ceil_div(tiles_max, tps);   // <= kDecodeMaxSplits for spans <= kDecodeMaxContext
   return p;
 }
 

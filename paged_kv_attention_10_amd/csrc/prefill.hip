@@ -72,9 +72,9 @@ using namespace pkv;
 
 extern "C" size_t paged_attn_prefill_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
                                                      int head_dim, int max_q_len,
-                                                     int max_context_len) {
+                                                     int max_context_len, int window) {
   (void)batch; (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)max_q_len;
-  (void)max_context_len;
+  (void)max_context_len; (void)window;
   return 0;
 }
 
@@ -86,7 +86,7 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
                                         int num_tokens, int max_q_len, int max_context_len,
                                         int batch, int num_q_heads, int num_kv_heads,
                                         int head_dim, int page_size, int num_pages, float scale,
-                                        void* out, int out_dtype, void* workspace,
+                                        int window, void* out, int out_dtype, void* workspace,
                                         size_t workspace_bytes, pkv_stream_t stream) {
   (void)workspace; (void)workspace_bytes;
   if (!k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens ||
@@ -94,7 +94,7 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
     return PKV_ERR_INVALID_ARG;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
       num_pages <= 0 || max_blocks_per_seq <= 0 || num_tokens < 0 || max_q_len < 0 ||
-      max_context_len < 0 || max_q_len > max_context_len ||
+      max_context_len < 0 || max_q_len > max_context_len || window < 0 ||
       (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE)
     return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
@@ -129,6 +129,7 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
   a.nrowblocks = ceil_div((long)max_q_len * a.group, kPrefillRowsPerBlock);
   a.scale_log2 = scale * kLog2e;
   a.skip_single = 0;
+  a.window = window;
   if (a.nrowblocks > 65535 || batch > 0x7fffffff) return PKV_ERR_INVALID_ARG;
 
   clear_launch_error();

@@ -46,6 +46,7 @@ struct PrefillArgs {
   int batch, hq, hkv, group, num_pages, nrowblocks;
   float scale_log2;
   int skip_single;   // mixed batch: chunks of one token are left to the decode path
+  int window;        // sliding window in tokens, 0 = the whole causal prefix
 };
 
 template <int D>
@@ -96,16 +97,27 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   const int wg_r0 = rb * kPrefillRowsPerBlock;
   if (wg_r0 >= rows_b) return;  // the whole workgroup, before any barrier
 
-  // the workgroup's key range and this wave's
+  // the workgroup's key range and this wave's.  With a sliding window of W
+  // tokens row position p sees keys (p - W, p]: the workgroup starts at the
+  // tile of its first row's window, and pages wholly before that window are
+  // never read.
   const int wg_last = min(rows_b - 1, wg_r0 + kPrefillRowsPerBlock - 1);
   const int ntiles = (P + wg_last / G + kPrefillTileKeys) / kPrefillTileKeys;
+  const int W = a.window;
+  const int wg_lo = W > 0 ? max(0, P + wg_r0 / G - W + 1) : 0;   // first key of the workgroup
+  const int t_first = wg_lo / kPrefillTileKeys;
+  const int p_first = wg_lo / kPage;                             // first page read
   const int r0 = wg_r0 + wave * kPrefillRowsPerWave;
   const int lim_min = P + r0 / G;      // smallest causal limit among the wave's rows
+  // largest window start among the wave's rows: tiles starting below it need
+  // the window mask
+  const int win_max = W > 0 ? P + min(rows_b - 1, r0 + kPrefillRowsPerWave - 1) / G - W + 1 : 0;
   const int row = r0 + col;
   const bool live = row < rows_b;
   const int pos = live ? row / G : 0;
   const int h = g * G + (live ? row - pos * G : 0);
   const int limit = live ? P + pos : -1;
+  const int wlo = W > 0 ? limit - W + 1 : 0;   // this row's first key
   const int npages = (ctx + kPage - 1) / kPage;
   const long qrow = ((long)(q0 + pos) * a.hq + h) * D;
 
@@ -141,8 +153,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     const int i = 64 * win + lane;
     return i < npages ? bt[i] : 0;
   };
-  int pid_cur = load_window(0);
-  int pid_next = ntiles > 16 ? load_window(1) : 0;
+  int pid_cur = load_window(t_first >> 4);
+  int pid_next = ntiles > (t_first | 15) + 1 ? load_window((t_first >> 4) + 1) : 0;
 
   // ---- tile copy: wave w moves page 4t + w of the tile (K rows swizzled,
   //      V^T block as is) into stage `stg`; pages past the context are not
@@ -157,12 +169,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     koff[j] = rr * L::kRow + ((slot ^ k_swizzle<D>(rr)) * 16);
   }
   auto issue_tile = [&](int t, int stg) {
-    if ((t & 15) == 0 && t > 0) {
+    if ((t & 15) == 0 && t > t_first) {
       pid_cur = pid_next;
       pid_next = load_window((t >> 4) + 1);
     }
     const int pi = 4 * t + wave;
-    if (pi < npages) {
+    if (pi < npages && pi >= p_first) {
       int pid = __builtin_amdgcn_readlane(pid_cur, pi & 63);
       if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
       const long blk = ((long)pid * a.hkv + g) * L::kPageBytes;
@@ -223,8 +235,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         for (int j = 0; j < 2; ++j)
           vfr[hf][db][j] = *reinterpret_cast<const u32x4*>(
               st + vaddr + (2 * hf + j) * L::kPageBytes + db * 32 * 32);
-    // keys at or past the context end may hold anything: zero their V
-    if (kb + 64 > ctx) {
+    // keys at or past the context end, or in pages not read because they
+    // lie wholly before the window, may hold anything: zero their V
+    if (kb + 64 > ctx || kb < kPage * p_first) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -232,7 +245,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
           const int key0 = kb + 32 * hf + 16 * j + 8 * hh;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const uint32_t m = (key0 + e >= ctx) ? ((e & 1) ? 0x0000ffffu : 0xffff0000u) : 0xffffffffu;
+            const bool out = key0 + e >= ctx || key0 + e < kPage * p_first;
+            const uint32_t m = out ? ((e & 1) ? 0x0000ffffu : 0xffff0000u) : 0xffffffffu;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) vfr[hf][db][j][e >> 1] &= m;
           }
@@ -249,6 +263,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (16 * (r >> 3) + (r & 7) > rel) s[hf][r] = -INFINITY;
+      }
+    }
+    if (kb < win_max) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int rel = wlo - (kb + 32 * hf + 8 * hh);     // smallest allowed 16*(r/8) + r%8
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + (r & 7) < rel) s[hf][r] = -INFINITY;
       }
     }
     float mt = s[0][0];
@@ -289,9 +312,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   };
 
   // ---- pipeline: tile t computes from LDS while tile t+1 is copied in
-  issue_tile(0, 0);
+  issue_tile(t_first, t_first & 1);
   __syncthreads();  // waits for this wave's copies, then for every wave's
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_first; t < ntiles; ++t) {
     if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
     const char* st = lds + (t & 1) * L::stage;
     const int kb = t * kPrefillTileKeys;

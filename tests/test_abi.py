@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2 == _lib.ABI_VERSION
     for code in range(6):
         assert lib.pkv_status_string(code).decode().startswith("PKV_")
     assert lib.pkv_status_string(99).decode() == "PKV_ERR_UNKNOWN"
@@ -40,15 +40,21 @@ def test_version_and_status_strings(lib):
 
 def test_decode_workspace_query_is_pure(lib):
     ws = lib.paged_attn_decode_workspace_bytes
-    assert ws(64, 12, 2, 128, 4096) == ws(64, 12, 2, 128, 4096) > 0
-    assert ws(384, 12, 12, 64, 1024) == 0          # contexts fit one partition
-    assert ws(0, 12, 2, 128, 4096) == 0            # invalid shapes -> 0
-    assert ws(4, 9, 2, 64, 200) == 0
-    assert ws(4, 9, 3, 96, 200) == 0
+    assert ws(64, 12, 2, 128, 4096, 0) == ws(64, 12, 2, 128, 4096, 0) > 0
+    assert ws(384, 12, 12, 64, 1024, 0) == 0          # contexts fit one partition
+    assert ws(0, 12, 2, 128, 4096, 0) == 0            # invalid shapes -> 0
+    assert ws(4, 9, 2, 64, 200, 0) == 0
+    assert ws(4, 9, 3, 96, 200, 0) == 0
+    assert ws(64, 12, 2, 128, 4096, -1) == 0          # negative window
     # more context never needs less workspace
-    sizes = [ws(16, 8, 1, 128, n) for n in (64, 512, 4096, 32768)]
+    sizes = [ws(16, 8, 1, 128, n, 0) for n in (64, 512, 4096, 32768)]
     assert sizes == sorted(sizes)
-    assert lib.paged_attn_prefill_workspace_bytes(8, 12, 2, 128, 512, 4096) == 0
+    # a window bounds the span the split plan covers
+    assert ws(16, 8, 1, 128, 32768, 1024) < ws(16, 8, 1, 128, 32768, 0)
+    assert ws(16, 8, 1, 128, 32768, 10**6) == ws(16, 8, 1, 128, 32768, 0)
+    # beyond the longest span without a window, within it with one
+    assert ws(4, 8, 1, 128, 1 << 20, 0) == 0 < ws(4, 8, 1, 128, 1 << 20, 4096)
+    assert lib.paged_attn_prefill_workspace_bytes(8, 12, 2, 128, 512, 4096, 0) == 0
 
 
 FAKE = 0x7f0000000000           # 16-byte aligned stand-in address, never dereferenced
@@ -56,7 +62,7 @@ FAKE = 0x7f0000000000           # 16-byte aligned stand-in address, never derefe
 
 def _decode(lib, **over):
     a = dict(q=FAKE, qd=0, k=FAKE, v=FAKE, ks=None, vs=None, kvd=1, bt=FAKE, mb=8, cl=FAKE,
-             mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125, out=FAKE, od=0,
+             mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125, win=0, out=FAKE, od=0,
              ws=FAKE, wsb=1 << 20, st=None)
     a.update(over)
     return lib.paged_attn_decode(*a.values())
@@ -65,7 +71,7 @@ def _decode(lib, **over):
 def _prefill(lib, **over):
     a = dict(q=FAKE, qd=1, k=FAKE, v=FAKE, ks=None, vs=None, kvd=1, bt=FAKE, mb=8, cl=FAKE,
              cu=FAKE, T=64, mql=32, mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125,
-             out=FAKE, od=0, ws=None, wsb=0, st=None)
+             win=0, out=FAKE, od=0, ws=None, wsb=0, st=None)
     a.update(over)
     return lib.paged_attn_prefill_chunk(*a.values())
 
@@ -73,7 +79,7 @@ def _prefill(lib, **over):
 def _mixed(lib, **over):
     a = dict(q=FAKE, qd=1, k=FAKE, v=FAKE, ks=None, vs=None, kvd=1, bt=FAKE, mb=8, cl=FAKE,
              cu=FAKE, T=64, mql=32, mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125,
-             out=FAKE, od=0, ws=FAKE, wsb=1 << 20, st=None)
+             win=0, out=FAKE, od=0, ws=FAKE, wsb=1 << 20, st=None)
     a.update(over)
     return lib.paged_attn_mixed(*a.values())
 
@@ -99,13 +105,14 @@ INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL = 1, 2, 3, 4
     ({"ks": FAKE, "vs": FAKE}, INVALID),                    # scales with a non-int8 KV
     ({"ps": 8}, UNSUPPORTED), ({"d": 96}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED),
     ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest context built
+    ({"win": -1}, INVALID),
     ({"q": FAKE + 4}, MISALIGNED), ({"v": FAKE + 8}, MISALIGNED), ({"out": FAKE + 2}, MISALIGNED),
     ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "ws": None, "wsb": 0, "mb": 256}, WS_SMALL),
     ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "wsb": 1024, "mb": 256}, WS_SMALL),
 ])
 def test_decode_rejects(lib, over, code):
     if code == WS_SMALL:
-        assert lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096) > 1024
+        assert lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096, 0) > 1024
     assert _decode(lib, **over) == code
 
 
@@ -115,7 +122,7 @@ def test_decode_rejects(lib, over, code):
     ({"T": -1}, INVALID), ({"hq": 3}, INVALID), ({"mcl": 200}, INVALID),
     ({"kvd": 0}, UNSUPPORTED), ({"kvd": 3, "ks": FAKE, "vs": FAKE}, UNSUPPORTED),
     ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED), ({"cu": FAKE + 4}, MISALIGNED),
-    ({"od": 3}, INVALID),
+    ({"od": 3}, INVALID), ({"win": -5}, INVALID),
 ])
 def test_prefill_rejects(lib, over, code):
     assert _prefill(lib, **over) == code
@@ -128,7 +135,7 @@ def test_prefill_rejects(lib, over, code):
     ({"kvd": 0}, UNSUPPORTED), ({"kvd": 3, "ks": FAKE, "vs": FAKE}, UNSUPPORTED),
     ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED),
     ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest split context
-    ({"cu": FAKE + 4}, MISALIGNED), ({"od": 3}, INVALID),
+    ({"cu": FAKE + 4}, MISALIGNED), ({"od": 3}, INVALID), ({"win": -1}, INVALID),
     ({"mcl": 4096, "mb": 256, "B": 64, "hq": 12, "hkv": 2, "d": 128, "mql": 1, "ws": None, "wsb": 0},
      WS_SMALL),
 ])
@@ -139,12 +146,13 @@ def test_mixed_rejects(lib, over, code):
 def test_mixed_workspace_follows_the_split_plan(lib):
     ws = lib.paged_attn_mixed_workspace_bytes
     # short chunks only: the one-token rows are planned as a decode call
-    dec = lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096)
-    assert ws(64, 12, 2, 128, 1, 4096) == ws(64, 12, 2, 128, 127, 4096) == dec > 0
+    dec = lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096, 0)
+    assert ws(64, 12, 2, 128, 1, 4096, 0) == ws(64, 12, 2, 128, 127, 4096, 0) == dec > 0
     # with long chunks: the fewest splits the context allows (none up to 4096 tokens)
-    assert ws(72, 12, 2, 128, 512, 4096) == 0
-    assert ws(8, 12, 2, 128, 512, 20000) > 0
-    assert ws(0, 12, 2, 128, 512, 4096) == 0
+    assert ws(72, 12, 2, 128, 512, 4096, 0) == 0
+    assert ws(8, 12, 2, 128, 512, 20000, 0) > 0
+    assert ws(8, 12, 2, 128, 512, 20000, 2048) == 0   # a window bounds the span
+    assert ws(0, 12, 2, 128, 512, 4096, 0) == 0
 
 
 def test_mixed_empty_call_is_noop(lib):

@@ -265,7 +265,8 @@ def test_error_codes_with_device_buffers(pkv):
     def call(**over):
         args = dict(q=P(q), qd=0, k=P(gc["k"]), v=P(gc["v"]), ks=None, vs=None, kvd=1, bt=P(bt),
                     mb=int(w.block_tables.shape[1]), cl=P(cl), mcl=20, B=1, hq=4, hkv=2, d=64,
-                    ps=16, np_=w.num_pages, sc=0.125, out=P(out), od=0, ws=None, wsb=0, st=None)
+                    ps=16, np_=w.num_pages, sc=0.125, win=0, out=P(out), od=0, ws=None, wsb=0,
+                    st=None)
         args.update(over)
         return lib.paged_attn_decode(*args.values())
 
@@ -278,6 +279,7 @@ def test_error_codes_with_device_buffers(pkv):
     assert call(kvd=3) == 1                       # int8 without scales
     assert call(qd=3) == 1                        # int8 query
     assert call(mcl=10000) == 1                   # beyond the block table
+    assert call(win=-1) == 1                      # negative window
     assert call(q=ctypes.c_void_p(q.data_ptr() + 4)) == 3
     assert call(mcl=20, B=1, hq=4, hkv=2) == 0
     torch.cuda.synchronize()

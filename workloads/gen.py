@@ -176,7 +176,58 @@ def _c5(seed):
                   meta={"desc": "paged decode, int8 KV + per-token-head fp32 scales, TinyLlama-1.1B shape, B=128, 32/4 heads, d=64"})
 
 
-CONFIGS = {"C1": (_c1, 1), "C2": (_c2, 2), "C3": (_c3, 3), "C4": (_c4, 4), "C5": (_c5, 5)}
+EVICTED = -1   # block-table entry of a page a window-bounded cache has recycled
+
+
+def _w1(seed):
+    """Decode with a sliding window over long contexts, laid out the way a
+    cache whose storage the window bounds holds it: only the pages that
+    overlap each sequence's window (its last `window` positions) are
+    allocated and drawn; block-table entries of earlier pages are EVICTED.
+    k/v/slot_mapping hold the window tokens only (token_offsets delimit each
+    sequence's), in position order.  Draw order: context lengths -> page
+    permutation -> q -> K -> V."""
+    window = 4096
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = rng.integers(16384, 65536, size=64, endpoint=True)
+    batch, hq, hkv, d = 64, 12, 2, 128
+    first = ctx - window
+    p0 = first // PAGE_SIZE
+    p1 = (ctx + PAGE_SIZE - 1) // PAGE_SIZE
+    needed = int((p1 - p0).sum())
+    num_pages = 20000
+    perm = rng.permutation(num_pages).astype(np.int32)
+    sentinel = int(perm[needed])
+    table_width = int(p1.max())
+    block_tables = np.full((batch, table_width), sentinel, dtype=np.int32)
+    offsets = np.zeros(batch + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(ctx - first)
+    slots = np.zeros(int(offsets[-1]), dtype=np.int64)
+    cursor = 0
+    for b in range(batch):
+        n = int(p1[b] - p0[b])
+        block_tables[b, :p0[b]] = EVICTED
+        block_tables[b, p0[b]:p1[b]] = perm[cursor:cursor + n]
+        cursor += n
+        t = np.arange(int(first[b]), int(ctx[b]), dtype=np.int64)
+        slots[offsets[b]:offsets[b + 1]] = (
+            block_tables[b, t // PAGE_SIZE].astype(np.int64) * PAGE_SIZE + t % PAGE_SIZE)
+    q = rng.standard_normal((batch, hq, d), dtype=np.float32)
+    k = rng.standard_normal((int(offsets[-1]), hkv, d), dtype=np.float32)
+    v = rng.standard_normal((int(offsets[-1]), hkv, d), dtype=np.float32)
+    return Workload(
+        name="W1", kind="decode", batch=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        kv_dtype="bf16", q_dtype="f32", out_dtype="f32", num_pages=num_pages,
+        sentinel_page=sentinel, context_lens=ctx.astype(np.int32),
+        q_lens=np.ones(batch, dtype=np.int32), cu_q_lens=np.arange(batch + 1, dtype=np.int32),
+        block_tables=block_tables, token_offsets=offsets, slot_mapping=slots, q=q, k=k, v=v,
+        scale=float(np.float32(1.0) / np.sqrt(np.float32(d))), seed=seed,
+        meta={"desc": "sliding-window decode, bf16 KV, Qwen2.5-1.5B shape, B=64, ctx U[16384,65536], window 4096, only window pages held",
+              "window": window, "first_pos": first.astype(np.int64)})
+
+
+CONFIGS = {"C1": (_c1, 1), "C2": (_c2, 2), "C3": (_c3, 3), "C4": (_c4, 4), "C5": (_c5, 5),
+           "W1": (_w1, 8)}
 
 
 def make_workload(name: str, seed: Optional[int] = None) -> Workload:
