@@ -41,13 +41,22 @@ notes):
   pinned properties are the rounding bound, the +-127 code at the absmax and
   sign symmetry.
 * bf16 from fp32: round to nearest even on the bit pattern; NaN stays NaN.
+* fp8: OCP FP8 E4M3 codes (1 sign, 4 exponent bits of bias 7, 3 mantissa
+  bits; largest finite 448; no infinities; S.1111.111 is NaN), the "FP8 KV
+  cache" the stylome.io "Classifier receipt" names beside INT8.  Symmetric
+  absmax per (token, KV head) like int8: ``scale = absmax / 448`` in IEEE
+  fp32, ``code = e4m3(x / scale)`` rounded to the nearest e4m3 value (ties
+  to even) after clamping to +-448; the sign bit is the sign of the fp32
+  ratio (so -0.0 and a negative value that rounds to zero store 0x80); an
+  all-zero vector gets scale 0 and codes 0.
 """
 from __future__ import annotations
 
 import numpy as np
 
 PAGE_SIZE = 16
-DTYPES = ("f32", "bf16", "f16", "i8")
+DTYPES = ("f32", "bf16", "f16", "i8", "fp8")
+E4M3_MAX = 448.0
 
 
 # ---------------------------------------------------------------- conversions
@@ -87,6 +96,52 @@ def quantize_int8(x):
     return codes, scale
 
 
+def f32_to_e4m3_bits(x) -> np.ndarray:
+    """Finite float32 values with |x| <= 448 -> OCP E4M3 codes (uint8), to
+    the nearest representable value with ties to even.  Normal values
+    2^e (1 + m/8) have e in [-6, 8]; below 2^-6 the grid is m * 2^-9."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    _, ex = np.frexp(a)                                  # a = frac * 2^ex, frac in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                           # exponent of a's binade, floored at -6
+    step = np.ldexp(1.0, e - 3)                          # grid spacing in that binade
+    q = np.minimum(np.rint(a / step) * step, E4M3_MAX)
+    _, qx = np.frexp(q)
+    qe = qx - 1
+    normal = q >= 2.0 ** -6
+    mant_normal = np.where(normal, q / np.ldexp(1.0, np.where(normal, qe, 0)) * 8 - 8, 0)
+    bits = np.where(normal, ((qe + 7) << 3) + mant_normal, q / 2.0 ** -9)
+    bits = bits.astype(np.int64) | np.where(np.signbit(x), 0x80, 0)
+    return bits.astype(np.uint8)
+
+
+def e4m3_bits_to_f64(bits) -> np.ndarray:
+    """OCP E4M3 codes -> float64 (exact); 0x7F / 0xFF are NaN."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    mag = np.where((b & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def quantize_fp8(x):
+    """Symmetric absmax FP8 (E4M3) over the last axis: scale in fp32, the
+    ratio x / scale in fp32, clamped to +-448, then rounded to E4M3.
+
+    Returns (codes uint8 [..., d], scale float32 [...])."""
+    x = np.asarray(x, dtype=np.float32)
+    absmax = np.max(np.abs(x), axis=-1)
+    scale = (absmax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    ratio = (x / safe[..., None]).astype(np.float32)
+    ratio = np.clip(ratio, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    codes = f32_to_e4m3_bits(ratio)
+    codes = np.where((scale > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, scale
+
+
 def storage_from_f32(x, dtype: str):
     """Convert float32 values to the cache's storage representation.
 
@@ -100,6 +155,8 @@ def storage_from_f32(x, dtype: str):
         return f32_to_f16(x)
     if dtype == "i8":
         return quantize_int8(x)
+    if dtype == "fp8":
+        return quantize_fp8(x)
     raise ValueError(dtype)
 
 
@@ -114,11 +171,14 @@ def upcast(stored, dtype: str, scales=None) -> np.ndarray:
     if dtype == "i8":
         return np.asarray(stored, dtype=np.int8).astype(np.float64) * \
             np.asarray(scales, dtype=np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return e4m3_bits_to_f64(stored) * np.asarray(scales, dtype=np.float32).astype(np.float64)
     raise ValueError(dtype)
 
 
 # ---------------------------------------------------------------- cache
-_STORE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "i8": np.int8}
+_STORE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "i8": np.int8, "fp8": np.uint8}
+SCALED = ("i8", "fp8")   # dtypes with per-(token, head) fp32 scales
 
 
 class PagedCache:
@@ -132,7 +192,7 @@ class PagedCache:
         st = _STORE[dtype]
         self.k = np.zeros((num_pages, num_kv_heads, PAGE_SIZE, head_dim), dtype=st)
         self.v = np.zeros((num_pages, num_kv_heads, head_dim, PAGE_SIZE), dtype=st)
-        if dtype == "i8":
+        if dtype in SCALED:
             self.k_scales = np.zeros((num_pages, num_kv_heads, PAGE_SIZE), np.float32)
             self.v_scales = np.zeros((num_pages, num_kv_heads, PAGE_SIZE), np.float32)
         else:
@@ -160,9 +220,9 @@ def ref_append(cache: PagedCache, k_new, v_new, slot_mapping) -> None:
     keep = slots >= 0
     slots, k_new, v_new = slots[keep], k_new[keep], v_new[keep]
     page, off = slots // PAGE_SIZE, slots % PAGE_SIZE
-    if cache.dtype == "i8":
-        kq, ks = quantize_int8(k_new)
-        vq, vs = quantize_int8(v_new)
+    if cache.dtype in SCALED:
+        kq, ks = storage_from_f32(k_new, cache.dtype)
+        vq, vs = storage_from_f32(v_new, cache.dtype)
         cache.k[page, :, off, :] = kq
         cache.v[page, :, :, off] = vq
         cache.k_scales[page, :, off] = ks

@@ -66,6 +66,14 @@ def _dense_stored(x_f32, dtype, O):
         return t.to(torch.bfloat16).double().numpy()
     if dtype == "f16":
         return t.to(torch.float16).double().numpy()
+    if dtype == "fp8":
+        # absmax scale in fp32, then torch's own E4M3 rounding of the ratio
+        x = np.asarray(x_f32, np.float32)
+        sc = (np.max(np.abs(x), axis=-1) / np.float32(448.0)).astype(np.float32)
+        safe = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
+        r = np.clip((x / safe[..., None]).astype(np.float32), -448, 448).astype(np.float32)
+        codes = torch.from_numpy(r).to(torch.float8_e4m3fn).double().numpy()
+        return np.where((sc > 0)[..., None], codes, 0.0) * sc.astype(np.float64)[..., None]
     codes, sc = O.quantize_int8(x_f32)
     return codes.astype(np.float64) * sc.astype(np.float64)[..., None]
 
@@ -117,7 +125,7 @@ def pin_bruteforce_prefill(O):
 
 
 def pin_sdpa_decode_all_dtypes(O):
-    for dtype in ("f32", "bf16", "f16", "i8"):
+    for dtype in ("f32", "bf16", "f16", "i8", "fp8"):
         w = custom_workload(context_lens=[16, 17, 33, 70], num_q_heads=6, num_kv_heads=2,
                             head_dim=16, kv_dtype=dtype, num_pages=24, seed=13)
         cache = _filled_cache(O, w)
@@ -545,6 +553,68 @@ def pin_window_special_cases(O):
         bt[b, :max(0, int(w.context_lens[b]) - W) // PS] = 10**7
     got = O.ref_decode(qd, c, bt, w.context_lens, w.scale, 4, window=W)
     assert np.array_equal(got, O.ref_decode(qd, c, w.block_tables, w.context_lens, w.scale, 4, window=W))
+
+
+# ------------------------------------------------------------------ fp8 (E4M3)
+def _e4m3_torch(v):
+    return torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def pin_fp8_encoding_matches_torch(O):
+    """E4M3 rounding against torch's float8_e4m3fn cast: every bf16 value in
+    [-448, 448], log-uniform fp32 draws, and the exact midpoints between
+    neighbouring E4M3 values (ties go to the even code)."""
+    b = np.arange(1 << 16, dtype=np.uint32) << 16
+    v = b.view(np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) <= 448)]
+    rng = np.random.default_rng(91)
+    r = (rng.standard_normal(100000) * np.exp(rng.uniform(-14, 6.1, 100000))).astype(np.float32)
+    r = np.clip(r, -448, 448)
+    codes = np.arange(0x7F, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)      # exact in fp32
+    for arr in (v, r, mids, -mids):
+        assert np.array_equal(O.f32_to_e4m3_bits(arr), _e4m3_torch(arr))
+
+
+def pin_fp8_decoding_matches_torch(O):
+    codes = np.arange(256, dtype=np.uint8)
+    finite = (codes & 0x7F) != 0x7F
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_bits_to_f64(codes)
+    assert np.array_equal(got[finite], ref[finite]) and np.all(np.isnan(got[~finite]))
+
+
+def pin_fp8_golden(O):
+    """Hand-derived: absmax 448 gives scale 1; 448 -> 0x7E (exponent field
+    15, mantissa 6), -1 -> 0xB8, 0.5 -> 0x30, 1e-3 -> 0x01 (subnormal
+    1e-3 * 2^9 = 0.512 rounds to 1), 0 -> 0x00, -0 -> 0x80, 3 -> 0x44,
+    17 -> 0x58 (17/2 = 8.5 ties to the even 8: 16 = 2^4)."""
+    x = np.array([[448, -1, 0.5, 1e-3, 0, -0.0, 3.0, 17.0]], np.float32)
+    codes, sc = O.quantize_fp8(x)
+    assert sc[0] == np.float32(1.0)
+    assert codes[0].tolist() == [0x7E, 0xB8, 0x30, 0x01, 0x00, 0x80, 0x44, 0x58]
+    z, zs = O.quantize_fp8(np.zeros((2, 8), np.float32))
+    assert np.all(z == 0) and np.all(zs == 0)
+
+
+def pin_fp8_bounds(O):
+    """Per element the stored value is within half a grid step of x: 2^-4
+    relative for ratios of 2^-6 and up, scale * 2^-10 below; the absmax
+    element stores +-448 * scale; codes are sign-symmetric."""
+    rng = np.random.default_rng(92)
+    x = (rng.standard_normal((300, 64)) * np.exp(rng.uniform(-20, 20, (300, 1)))).astype(np.float32)
+    codes, sc = O.quantize_fp8(x)
+    got = O.e4m3_bits_to_f64(codes) * sc.astype(np.float64)[:, None]
+    xd = x.astype(np.float64)
+    s = sc.astype(np.float64)[:, None]
+    bound = np.maximum(np.abs(xd) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(np.abs(got - xd) <= bound)
+    am = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(O.e4m3_bits_to_f64(codes[np.arange(300), am])) == 448.0)
+    c2, s2 = O.quantize_fp8(-x)
+    assert np.array_equal(s2, sc) and np.array_equal(c2 ^ 0x80, codes)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -47,6 +47,15 @@ MUTANTS = [
      "            if window < 0:\n                s = np.where("),
     ("window_prefill_first_key_late", "lo = max(0, P - window + 1) if window > 0 else 0",
      "lo = max(0, P - window + 2) if window > 0 else 0"),
+    ("fp8_scale_240", "(absmax / np.float32(E4M3_MAX))", "(absmax / np.float32(240.0))"),
+    ("fp8_truncates", "q = np.minimum(np.rint(a / step) * step, E4M3_MAX)",
+     "q = np.minimum(np.floor(a / step) * step, E4M3_MAX)"),
+    ("fp8_bias_8", "bits = np.where(normal, ((qe + 7) << 3) + mant_normal, q / 2.0 ** -9)",
+     "bits = np.where(normal, ((qe + 8) << 3) + mant_normal, q / 2.0 ** -9)"),
+    ("fp8_subnormal_grid", "e = np.maximum(ex - 1, -6)", "e = np.maximum(ex - 1, -7)"),
+    ("fp8_two_mantissa_bits", "step = np.ldexp(1.0, e - 3)", "step = np.ldexp(1.0, e - 2)"),
+    ("fp8_dequant_unscaled", "return e4m3_bits_to_f64(stored) * np.asarray(scales, dtype=np.float32).astype(np.float64)",
+     "return e4m3_bits_to_f64(stored)"),
     ("rope_turns_backwards", "ra = a * c - b * s\n    rb = b * c + a * s",
      "ra = a * c + b * s\n    rb = b * c - a * s"),
     ("rope_not_a_rotation", "rb = b * c + a * s", "rb = b * c - a * s"),
