@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-ELEM = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1}
+ELEM = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "fp8": 1}
 DESC = {
     "C1": "paged decode, fp32 q/KV/out, batch 4, 9 q / 3 KV heads, head_dim 64, ctx {17,64,133,200}",
     "C2": "paged decode, bf16 KV + fp32 accumulation, Qwen2.5-1.5B shape: batch 64, 12 q / 2 KV heads, head_dim 128, ctx U[512,4096], 20k-page pool",
@@ -46,6 +46,7 @@ DESC = {
     "C5": "paged decode, int8 KV + per-token-head fp32 scales, TinyLlama-1.1B shape: batch 128, 32 q / 4 KV heads, head_dim 64, ctx 2048",
     "M1": "mixed batch in one call: the C2 decode batch (64 one-token chunks, ctx U[512,4096]) and the C4 chunks (8 x 512 tokens), 12 q / 2 KV heads, head_dim 128, bf16",
     "R1": "append with RoPE on K and q (rotate-half, theta 1e6), the C4 chunks' 4096 new tokens, bf16 K/V/q in and bf16 cache, 12 q / 2 KV heads, head_dim 128",
+    "F1": "paged decode, FP8 E4M3 KV + per-token-head fp32 scales, the C2 draw (Qwen2.5-1.5B shape: batch 64, 12 q / 2 KV heads, head_dim 128, ctx U[512,4096])",
     "W1": "sliding-window paged decode, bf16 KV, Qwen2.5-1.5B shape: batch 64, 12 q / 2 KV heads, head_dim 128, ctx U[16384,65536], window 4096, only the window's pages held (earlier block-table entries evicted)",
     "M2": "decode-heavy mixed batch in one call: the C2 decode batch (64 one-token chunks, ctx U[512,4096]) and 4 chunks of 64 tokens over 1024-token prefixes, 12 q / 2 KV heads, head_dim 128, bf16",
 }
@@ -62,7 +63,7 @@ def effective_kv_bytes(w) -> int:
     ctx = w.context_lens.astype(np.int64)
     tok = int((np.minimum(ctx, win) if win else ctx).sum())
     b = tok * w.num_kv_heads * w.head_dim * 2 * ELEM[w.kv_dtype]
-    if w.kv_dtype == "i8":
+    if w.kv_dtype in ("i8", "fp8"):
         b += tok * w.num_kv_heads * 2 * 4
     return b
 
@@ -117,11 +118,12 @@ class Gpu:
 
     def pool(self, w):
         torch = self.torch
-        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i8": torch.int8}[w.kv_dtype]
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i8": torch.int8,
+              "fp8": torch.float8_e4m3fn}[w.kv_dtype]
         k = torch.zeros((w.num_pages, w.num_kv_heads, 16, w.head_dim), dtype=dt, device=self.dev)
         v = torch.zeros((w.num_pages, w.num_kv_heads, w.head_dim, 16), dtype=dt, device=self.dev)
         ks = vs = None
-        if w.kv_dtype == "i8":
+        if w.kv_dtype in ("i8", "fp8"):
             ks = torch.zeros((w.num_pages, w.num_kv_heads, 16), dtype=torch.float32, device=self.dev)
             vs = torch.zeros_like(ks)
         return k, v, ks, vs
@@ -433,21 +435,21 @@ def main():
                     help="seconds of oracle CPU work for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of workloads to run (C1..C5, M1, M2, R1, W1); default all")
+                    help="comma list of workloads to run (C1..C5, M1, M2, R1, W1, F1); default all")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2", "R1",
-                                                        "W1"}
+                                                        "W1", "F1"}
 
     g = Gpu()
     extras = {}
     head = None
     if "C2" in only:
         w2, head, out2 = bench_decode(g, "C2", args.steps, args.warmup)
-    for name in ("C3", "C5", "C1", "W1"):
+    for name in ("C3", "C5", "C1", "W1", "F1"):
         if name in only:
             _, r, _ = bench_decode(g, name, args.steps, args.warmup)
             r["roofline"] = {"bound": "hbm", "achieved": r["decode_call_gbs"], "peak": HBM_PEAK_GBS,

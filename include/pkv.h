@@ -11,10 +11,11 @@
  * "Current Status", table "Model architecture support", row "Chunked
  * prefill"; Tiny-LLM "Project Status", supported-features list).  Query heads
  * share KV heads in groups (GQA/MQA; TinyLoop table "Model architecture
- * support", row "GQA").  KV storage is fp32, bf16, fp16 or int8 with
- * per-token-per-head fp32 scales (Tiny-LLM "Project Status", dtype-contract
- * paragraph; mini-llm README hardware table, FP16 KV cache; TinyLoop table
- * "KV cache modes", row "INT8 KV cache").
+ * support", row "GQA").  KV storage is fp32, bf16, fp16, or int8 or FP8
+ * (E4M3) codes with per-token-per-head fp32 scales (Tiny-LLM "Project
+ * Status", dtype-contract paragraph; mini-llm README hardware table, FP16 KV
+ * cache; TinyLoop table "KV cache modes", row "INT8 KV cache"; stylome.io
+ * "Classifier receipt", KV cache point: INT8 or FP8 KV cache).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -29,7 +30,7 @@
  * Cache layout (page size 16, the only size built):
  *   k_cache   [num_pages][num_kv_heads][16][head_dim]   token-major page
  *   v_cache   [num_pages][num_kv_heads][head_dim][16]   token index innermost
- *   k_scales, v_scales [num_pages][num_kv_heads][16] float32 (int8 only)
+ *   k_scales, v_scales [num_pages][num_kv_heads][16] float32 (int8 and FP8 only)
  * Token t of sequence b lives in page block_tables[b][t / 16] at offset
  * t % 16.  The V page is stored with tokens innermost so that the PV
  * contraction (over tokens) reads contiguous runs.
@@ -57,8 +58,10 @@ extern "C" {
 #define PKV_ABI_VERSION 2
 #define PKV_PAGE_SIZE 16
 
-/* Element types.  PKV_BF16 is bfloat16 bits, PKV_I8 is int8 codes (KV only). */
-enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_F16 = 2, PKV_I8 = 3 };
+/* Element types.  PKV_BF16 is bfloat16 bits; PKV_I8 (int8 codes) and PKV_FP8
+ * (OCP FP8 E4M3 codes: bias 7, largest finite 448) are KV-only and carry
+ * per-(token, KV head) fp32 scales. */
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_F16 = 2, PKV_I8 = 3, PKV_FP8 = 4 };
 
 /* Status codes. */
 enum {
@@ -93,15 +96,18 @@ const char* pkv_status_string(int status);
  *                  slot >= num_pages*16 is skipped too.  Two tokens with the
  *                  same slot in one call leave either one (undefined which).
  *   k_cache, v_cache  the pool (layout above), dtype cache_dtype; written.
- *   k_scales, v_scales  required (non-NULL) iff cache_dtype == PKV_I8, and
- *                  must be NULL otherwise; written.
+ *   k_scales, v_scales  required (non-NULL) iff cache_dtype is PKV_I8 or
+ *                  PKV_FP8, and must be NULL otherwise; written.
  *
  * Conversions: fp32 is copied bit for bit; fp16 and bf16 round to nearest
  * even (fp16 keeps subnormals; a bf16 NaN stays NaN); int8 is symmetric
  * absmax per (token, KV head): scale = absmax/127 in IEEE fp32, code =
  * clamp(rint(x/scale), -127, 127) with ties to even, scale 0 and codes 0 for
- * an all-zero vector; the int8 result for a vector holding inf or NaN is
- * unspecified.  num_tokens == 0 is a no-op returning PKV_OK.
+ * an all-zero vector; FP8 likewise with scale = absmax/448 and code = the
+ * E4M3 value nearest to clamp(x/scale, -448, 448) (ties to even; the sign
+ * bit is that of the fp32 ratio, so -0 stores 0x80).  The int8 and FP8
+ * results for a vector holding inf or NaN are unspecified.  num_tokens == 0
+ * is a no-op returning PKV_OK.
  */
 int paged_kv_append(const void* k_new, const void* v_new, int new_dtype,
                     const int64_t* slot_mapping, int num_tokens,
@@ -169,7 +175,7 @@ int paged_kv_append_rope(const void* k_new, const void* v_new, int new_dtype,
  *
  *   q              [batch][num_q_heads][head_dim], dtype q_dtype (F32/BF16/F16).
  *   k_cache, v_cache, k_scales, v_scales, kv_dtype   the pool (layout above);
- *                  scales non-NULL iff kv_dtype == PKV_I8.
+ *                  scales non-NULL iff kv_dtype is PKV_I8 or PKV_FP8.
  *   block_tables   [batch][max_blocks_per_seq] int32 page ids; entries past a
  *                  sequence's last page are never read.
  *   context_lens   [batch] int32, each in [0, max_context_len].

@@ -4,7 +4,7 @@ The compute lives in libpkv.so (hand-written HIP); this package only binds
 it.  Importing the package loads the library and fails if it is not built.
 """
 from ._lib import (  # noqa: F401
-    BF16, F16, F32, I8, PAGE_SIZE, PkvError, load_library, paged_attn_decode,
+    BF16, F16, F32, FP8, I8, PAGE_SIZE, PkvError, load_library, paged_attn_decode,
     paged_attn_decode_workspace_bytes, paged_attn_mixed, paged_attn_mixed_workspace_bytes,
     paged_attn_prefill_chunk, paged_attn_prefill_workspace_bytes, paged_kv_append,
     paged_kv_append_rope,

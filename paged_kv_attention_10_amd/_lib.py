@@ -17,9 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "pkv.h")
 
-F32, BF16, F16, I8 = 0, 1, 2, 3
+F32, BF16, F16, I8, FP8 = 0, 1, 2, 3, 4
 PAGE_SIZE = 16
-_TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8}
+_TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8,
+               torch.float8_e4m3fn: FP8}
 
 _c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 

@@ -199,7 +199,7 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
   __syncthreads();
 
   const int segs = 2 * a.hkv * NSEG;
-  const int ces = a.cache_dtype == PKV_F32 ? 4 : a.cache_dtype == PKV_I8 ? 1 : 2;
+  const int ces = a.cache_dtype == PKV_F32 ? 4 : kv_scaled(a.cache_dtype) ? 1 : 2;
   for (int t = threadIdx.x; t < tpb * segs; t += kAppendThreads) {
     // a row's NSEG lanes are consecutive and aligned and share a token, so
     // the int8 shuffle stays inside a group of lanes active together
@@ -227,20 +227,28 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
 
     const long head = page * a.hkv + h;
     uint32_t bits[16];
-    if (a.cache_dtype == PKV_I8) {
+    if (kv_scaled(a.cache_dtype)) {
       float am = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(x[j]));
 #pragma unroll
       for (int m = 1; m < NSEG; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
-      const float sc = am / 127.0f;
+      if (a.cache_dtype == PKV_I8) {
+        const float sc = am / 127.0f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float code = 0.f;
-        if (sc > 0.f) code = fminf(fmaxf(rintf(x[j] / sc), -127.f), 127.f);
-        bits[j] = (uint32_t)(int)code & 0xffu;
+        for (int j = 0; j < 16; ++j) {
+          float code = 0.f;
+          if (sc > 0.f) code = fminf(fmaxf(rintf(x[j] / sc), -127.f), 127.f);
+          bits[j] = (uint32_t)(int)code & 0xffu;
+        }
+        if (s == 0) (is_v ? a.v_scales : a.k_scales)[head * kPage + off] = sc;
+      } else {
+        const float sc = am / 448.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          bits[j] = sc > 0.f ? f32_to_e4m3_bits(fminf(fmaxf(x[j] / sc, -448.f), 448.f)) : 0u;
+        if (s == 0) (is_v ? a.v_scales : a.k_scales)[head * kPage + off] = sc;
       }
-      if (s == 0) (is_v ? a.v_scales : a.k_scales)[head * kPage + off] = sc;
       if (!is_v) {
         int8_t* dst = static_cast<int8_t*>(a.k_cache) + (head * kPage + off) * D;
         *reinterpret_cast<u32x2*>(dst + c0) =
@@ -326,7 +334,7 @@ static int append_launch(AppendArgs& a, int head_dim, bool rope, pkv_stream_t st
     return (int)(t < 1 ? 1 : t > kMaxTokensPerBlock ? kMaxTokensPerBlock : t);
   };
   a.kv_tokens_per_block = tokens_per_block(2L * a.hkv * nseg);
-  const int ces = a.cache_dtype == PKV_F32 ? 4 : a.cache_dtype == PKV_I8 ? 1 : 2;
+  const int ces = a.cache_dtype == PKV_F32 ? 4 : kv_scaled(a.cache_dtype) ? 1 : 2;
   a.v_via_lds = (long)a.kv_tokens_per_block * a.hkv * head_dim * ces <= kVTileBytes &&
                 a.kv_tokens_per_block > 1;
   const long kvb = ((long)a.num_tokens + a.kv_tokens_per_block - 1) / a.kv_tokens_per_block;
@@ -386,7 +394,7 @@ extern "C" int paged_kv_append(const void* k_new, const void* v_new, int new_dty
                                pkv_stream_t stream) {
   if (num_tokens < 0 || num_pages <= 0 || num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(new_dtype) || !kv_dtype_ok(cache_dtype)) return PKV_ERR_INVALID_ARG;
-  if ((cache_dtype == PKV_I8) != (k_scales != nullptr) || (cache_dtype == PKV_I8) != (v_scales != nullptr))
+  if (kv_scaled(cache_dtype) != (k_scales != nullptr) || kv_scaled(cache_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PKV_OK;
@@ -410,7 +418,7 @@ extern "C" int paged_kv_append_rope(const void* k_new, const void* v_new, int ne
                                     pkv_stream_t stream) {
   if (num_tokens < 0 || num_pages <= 0 || num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(new_dtype) || !kv_dtype_ok(cache_dtype)) return PKV_ERR_INVALID_ARG;
-  if ((cache_dtype == PKV_I8) != (k_scales != nullptr) || (cache_dtype == PKV_I8) != (v_scales != nullptr))
+  if (kv_scaled(cache_dtype) != (k_scales != nullptr) || kv_scaled(cache_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (rope_style != PKV_ROPE_HALF && rope_style != PKV_ROPE_INTERLEAVED) return PKV_ERR_INVALID_ARG;
   if (!(rope_theta > 0.f) || !isfinite(rope_theta)) return PKV_ERR_INVALID_ARG;

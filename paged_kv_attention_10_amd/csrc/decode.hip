@@ -65,7 +65,8 @@ static void dispatch_kv(int kv, const DecodeArgs& a, pkv_stream_t stream) {
     case PKV_F32: launch_decode<D, PKV_F32>(a, stream); break;
     case PKV_BF16: launch_decode<D, PKV_BF16>(a, stream); break;
     case PKV_F16: launch_decode<D, PKV_F16>(a, stream); break;
-    default: launch_decode<D, PKV_I8>(a, stream); break;
+    case PKV_I8: launch_decode<D, PKV_I8>(a, stream); break;
+    default: launch_decode<D, PKV_FP8>(a, stream); break;
   }
 }
 
@@ -100,7 +101,7 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
     return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
     return PKV_ERR_INVALID_ARG;
-  if ((kv_dtype == PKV_I8) != (k_scales != nullptr) || (kv_dtype == PKV_I8) != (v_scales != nullptr))
+  if (kv_scaled(kv_dtype) != (k_scales != nullptr) || kv_scaled(kv_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim) ||
       !decode_span_supported(max_context_len, window))

@@ -49,14 +49,17 @@ __device__ __forceinline__ int checked_ctx(int raw, int max_ctx, int max_blocks,
   return raw;
 }
 
+// KV dtypes stored as one-byte codes with per-(token, head) scales.
+constexpr bool kv_code8(int kv) { return kv == PKV_I8 || kv == PKV_FP8; }
+
 template <int D, int KV>
 struct DecodeTile {
   // K fragments: 16-byte loads per MFMA row-half u.
-  static constexpr int KL = (KV == PKV_F32) ? D / 16 : (KV == PKV_I8 ? D / 64 : D / 32);
+  static constexpr int KL = (KV == PKV_F32) ? D / 16 : (kv_code8(KV) ? D / 64 : D / 32);
   u32x4 k[2][KL];
   // V^T fragments, one per 16-row block of d.
-  u32x4 v[(KV == PKV_I8) ? 1 : D / 16][(KV == PKV_F32) ? 2 : 1];
-  u32x2 v8[(KV == PKV_I8) ? D / 16 : 1];
+  u32x4 v[kv_code8(KV) ? 1 : D / 16][(KV == PKV_F32) ? 2 : 1];
+  u32x2 v8[kv_code8(KV) ? D / 16 : 1];
   f32x4 ks[2], vs[2];
 };
 
@@ -76,7 +79,7 @@ __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs
   const int r = lane & 15, kg = lane >> 4;
   const int page_k = (r < 8) ? pa : pb;
   const int rows_tok = 8 * ((r >> 2) & 1) + (r & 3);  // + 4*u
-  constexpr int ES = (KV == PKV_F32) ? 4 : (KV == PKV_I8 ? 1 : 2);
+  constexpr int ES = (KV == PKV_F32) ? 4 : (kv_code8(KV) ? 1 : 2);
   const char* kbase = static_cast<const char*>(a.k_cache) +
                       ((long)page_k * a.hkv + g) * (long)(kPage * D) * ES;
 #pragma unroll
@@ -86,7 +89,7 @@ __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs
     for (int s = 0; s < DecodeTile<D, KV>::KL; ++s) {
       int d0;
       if constexpr (KV == PKV_F32) d0 = 16 * s + 4 * kg;
-      else if constexpr (KV == PKV_I8) d0 = 64 * s + 16 * kg;
+      else if constexpr (kv_code8(KV)) d0 = 64 * s + 16 * kg;
       else d0 = 32 * s + 8 * kg;
       t.k[u][s] = *reinterpret_cast<const u32x4*>(row + (long)d0 * ES);
     }
@@ -97,7 +100,7 @@ __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs
 #pragma unroll
   for (int blk = 0; blk < D / 16; ++blk) {
     const char* p = vbase + ((long)(16 * blk + r) * kPage + 8 * (kg & 1)) * ES;
-    if constexpr (KV == PKV_I8) {
+    if constexpr (kv_code8(KV)) {
       t.v8[blk] = *reinterpret_cast<const u32x2*>(p);
     } else if constexpr (KV == PKV_F32) {
       t.v[blk][0] = *reinterpret_cast<const u32x4*>(p);
@@ -106,7 +109,7 @@ __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs
       t.v[blk][0] = *reinterpret_cast<const u32x4*>(p);
     }
   }
-  if constexpr (KV == PKV_I8) {
+  if constexpr (kv_code8(KV)) {
     // scales of the 8 tokens 8*kg..8*kg+7 this lane holds scores for
     const long sidx = ((long)page_v * a.hkv + g) * kPage + 8 * (kg & 1);
     t.ks[0] = *reinterpret_cast<const f32x4*>(a.k_scales + sidx);
@@ -137,7 +140,9 @@ template <int D, int KV>
 __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char* smem, int split,
                                                       int gy, int b) {
   constexpr bool kF32 = (KV == PKV_F32);
-  constexpr bool kI8 = (KV == PKV_I8);
+  constexpr bool kI8 = kv_code8(KV);   // int8 or FP8 codes, exact in fp16
+  // an FP8 code converts to 2^-8 times its value; the 2^8 goes on the scales
+  constexpr float kCodeScale = (KV == PKV_FP8) ? 256.0f : 1.0f;
   constexpr bool kBF16 = (KV == PKV_BF16);
   using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
   constexpr int NSTEP = kF32 ? D / 4 : D / 32;    // QK MFMA k-steps
@@ -266,7 +271,9 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             f16x8 kf;
-            i8x8_to_f16x8(u32x2{cur.k[u][s2i][2 * h], cur.k[u][s2i][2 * h + 1]}, kf);
+            const u32x2 codes = u32x2{cur.k[u][s2i][2 * h], cur.k[u][s2i][2 * h + 1]};
+            if constexpr (KV == PKV_FP8) fp8x8_to_f16x8(codes, kf);
+            else i8x8_to_f16x8(codes, kf);
             sacc = mfma16x16x32(kf, qhi[2 * s2i + h], sacc);
             sacc = mfma16x16x32(kf, qlo[2 * s2i + h], sacc);
           }
@@ -291,7 +298,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = s2[e >> 2][e & 3] * a.scale_log2;
-      if constexpr (kI8) x *= cur.ks[e >> 2][e & 3];
+      if constexpr (kI8) x *= cur.ks[e >> 2][e & 3] * kCodeScale;
       sc[e] = x;
     }
     if (partial) {
@@ -339,7 +346,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float x = p[e];
-        if constexpr (kI8) x = (tok0 + e < ctx && tok0 + e >= lo) ? x * cur.vs[e >> 2][e & 3] : 0.f;
+        if constexpr (kI8)
+          x = (tok0 + e < ctx && tok0 + e >= lo) ? x * (cur.vs[e >> 2][e & 3] * kCodeScale) : 0.f;
         pv[e] = x;
       }
       // V of tokens at or past the context end or before the window may
@@ -365,7 +373,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
         H8 vf;
         if constexpr (kI8) {
           f16x8 tmp;
-          i8x8_to_f16x8(cur.v8[blk], tmp);
+          if constexpr (KV == PKV_FP8) fp8x8_to_f16x8(cur.v8[blk], tmp);
+          else i8x8_to_f16x8(cur.v8[blk], tmp);
           vf = tmp;
         } else {
           u32x4 wv = cur.v[blk][0];

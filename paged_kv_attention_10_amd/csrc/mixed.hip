@@ -113,7 +113,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
     return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
     return PKV_ERR_INVALID_ARG;
-  if ((kv_dtype == PKV_I8) != (k_scales != nullptr) || (kv_dtype == PKV_I8) != (v_scales != nullptr))
+  if (kv_scaled(kv_dtype) != (k_scales != nullptr) || kv_scaled(kv_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim) ||
       !decode_span_supported(max_context_len, window))

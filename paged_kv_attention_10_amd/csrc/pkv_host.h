@@ -11,7 +11,8 @@ namespace pkv {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool head_dim_built(int d) { return d == 64 || d == 128; }
 inline bool io_dtype_ok(int dt) { return dt == PKV_F32 || dt == PKV_BF16 || dt == PKV_F16; }
-inline bool kv_dtype_ok(int dt) { return io_dtype_ok(dt) || dt == PKV_I8; }
+__host__ __device__ inline bool kv_scaled(int dt) { return dt == PKV_I8 || dt == PKV_FP8; }
+inline bool kv_dtype_ok(int dt) { return io_dtype_ok(dt) || kv_scaled(dt); }
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 // Clears any stale error, so the check after a launch sees only ours.

@@ -99,7 +99,7 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
     return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
     return PKV_ERR_INVALID_ARG;
-  if ((kv_dtype == PKV_I8) != (k_scales != nullptr) || (kv_dtype == PKV_I8) != (v_scales != nullptr))
+  if (kv_scaled(kv_dtype) != (k_scales != nullptr) || kv_scaled(kv_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16) return PKV_ERR_UNSUPPORTED;

@@ -12,8 +12,10 @@ import oracle
 from workloads import custom_workload, make_workload
 
 PS = 16
-TOL = {"f32": 2e-5, "bf16": 1e-2, "f16": 1e-2, "i8": 1e-2}
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i8": torch.int8}
+TOL = {"f32": 2e-5, "bf16": 1e-2, "f16": 1e-2, "i8": 1e-2, "fp8": 1e-2}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i8": torch.int8,
+            "fp8": torch.float8_e4m3fn}
+SCALED = ("i8", "fp8")
 
 
 def say(*a):
@@ -24,12 +26,16 @@ def say(*a):
 def np_to_gpu(a: np.ndarray) -> torch.Tensor:
     if a.dtype == np.uint16:          # bf16 bit patterns
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    if a.dtype == np.uint8:           # FP8 E4M3 codes
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda().view(torch.float8_e4m3fn)
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
 def gpu_to_np_bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
     return t.cpu().numpy()
 
 
@@ -68,11 +74,14 @@ def poisoned_gpu_cache(cache, used):
     elif cache.dtype == "i8":
         k = np.where(mk, k, np.int8(127))
         v = np.where(mv, v, np.int8(127))
+    elif cache.dtype == "fp8":
+        k = np.where(mk, k, np.uint8(0x7F))     # the E4M3 NaN code
+        v = np.where(mv, v, np.uint8(0x7F))
     else:
         k = np.where(mk, k, np.array(np.nan, dtype=k.dtype))
         v = np.where(mv, v, np.array(np.nan, dtype=v.dtype))
     out = {"k": np_to_gpu(k), "v": np_to_gpu(v), "ks": None, "vs": None}
-    if cache.dtype == "i8":
+    if cache.dtype in SCALED:
         ms = used[:, None, :]
         out["ks"] = np_to_gpu(np.where(ms, cache.k_scales, np.float32(np.nan)))
         out["vs"] = np_to_gpu(np.where(ms, cache.v_scales, np.float32(np.nan)))

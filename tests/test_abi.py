@@ -102,6 +102,7 @@ INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL = 1, 2, 3, 4
     ({"mcl": 129}, INVALID), ({"mcl": -1}, INVALID), ({"mb": 0}, INVALID),
     ({"qd": 3}, INVALID), ({"od": 7}, INVALID), ({"kvd": 4}, INVALID),
     ({"kvd": 3}, INVALID),                                  # int8 KV without scales
+    ({"kvd": 4}, INVALID), ({"kvd": 5}, INVALID),           # FP8 KV without scales, no such dtype
     ({"ks": FAKE, "vs": FAKE}, INVALID),                    # scales with a non-int8 KV
     ({"ps": 8}, UNSUPPORTED), ({"d": 96}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED),
     ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest context built
@@ -121,6 +122,7 @@ def test_decode_rejects(lib, over, code):
     ({"q": None}, INVALID), ({"cu": None}, INVALID), ({"mql": 200}, INVALID),
     ({"T": -1}, INVALID), ({"hq": 3}, INVALID), ({"mcl": 200}, INVALID),
     ({"kvd": 0}, UNSUPPORTED), ({"kvd": 3, "ks": FAKE, "vs": FAKE}, UNSUPPORTED),
+    ({"kvd": 4, "ks": FAKE, "vs": FAKE}, UNSUPPORTED),
     ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED), ({"cu": FAKE + 4}, MISALIGNED),
     ({"od": 3}, INVALID), ({"win": -5}, INVALID),
 ])
@@ -162,6 +164,7 @@ def test_mixed_empty_call_is_noop(lib):
 @pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
 @pytest.mark.parametrize("over,code", [
     ({"T": -1}, INVALID), ({"nd": 3}, INVALID), ({"cd": 5}, INVALID), ({"cd": 3}, INVALID),
+    ({"cd": 4}, INVALID), ({"nd": 4}, INVALID),
     ({"np_": 0}, INVALID), ({"ps": 8}, UNSUPPORTED), ({"d": 32}, UNSUPPORTED),
     ({"slots": None}, INVALID), ({"kc": FAKE + 4}, MISALIGNED), ({"slots": FAKE + 4}, MISALIGNED),
 ])

@@ -32,7 +32,7 @@ def _lengths(rng, n, hi):
 @pytest.mark.parametrize("it", range(24))
 def test_decode_fuzz(pkv, it):
     rng = np.random.default_rng(1000 + it)
-    kv = ["f32", "bf16", "f16", "i8"][it % 4]
+    kv = ["f32", "bf16", "f16", "i8", "fp8"][it % 5]
     d = [64, 128][(it // 4) % 2]
     hkv = int(rng.choice([1, 2, 3, 4]))
     G = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 20]))

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (TOL, TORCH_DT, config_case, gpu_to_np_bits, np_to_gpu, oracle_cache,
+from gpu_helpers import (SCALED, TOL, TORCH_DT, config_case, gpu_to_np_bits, np_to_gpu, oracle_cache,
                          poisoned_gpu_cache, q_exact_values, q_tensor, run_decode, run_prefill,
                          say, small_decode, small_prefill, to_f64, used_slot_mask)
 from workloads import custom_workload, make_workload
@@ -36,7 +36,7 @@ def _decode_check(pkv, w, cache, q_dtype="f32", out_dtype=torch.float32, tol=Non
 
 
 # ------------------------------------------------------------------ append
-@pytest.mark.parametrize("cache_dtype", ["f32", "bf16", "f16", "i8"])
+@pytest.mark.parametrize("cache_dtype", ["f32", "bf16", "f16", "i8", "fp8"])
 @pytest.mark.parametrize("new_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_append_bit_exact(pkv, cache_dtype, new_dtype, d):
@@ -48,8 +48,8 @@ def test_append_bit_exact(pkv, cache_dtype, new_dtype, d):
     k[0, 0, :8] = [0.0, -0.0, 2.0**-25, 3 * 2.0**-25, 6e-8, 65520.0, 1.00390625, -1.01171875]
     v[1, 1, :] = 0.0
     k[2, 0, :4] = [np.float32(1e-40), -1e-41, 7e4, -1e5]
-    if cache_dtype == "i8":
-        # int8 quantization is specified for finite vectors only; keep the
+    if cache_dtype in SCALED:
+        # int8 / FP8 quantization is specified for finite vectors only; keep the
         # fp16-overflow values out of its input
         k[0, 0, 5] = 60000.0
         k[2, 0, 2:4] = [6e4, -5e4]
@@ -60,18 +60,18 @@ def test_append_bit_exact(pkv, cache_dtype, new_dtype, d):
     host = oracle.PagedCache(w.num_pages, 2, d, cache_dtype)
     host.k.view(np.uint8)[:] = 0xA5
     host.v.view(np.uint8)[:] = 0xA5
-    if cache_dtype == "i8":
+    if cache_dtype in SCALED:
         host.k_scales.view(np.uint8)[:] = 0xA5
         host.v_scales.view(np.uint8)[:] = 0xA5
     gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
-    gks = np_to_gpu(host.k_scales) if cache_dtype == "i8" else None
-    gvs = np_to_gpu(host.v_scales) if cache_dtype == "i8" else None
+    gks = np_to_gpu(host.k_scales) if cache_dtype in SCALED else None
+    gvs = np_to_gpu(host.v_scales) if cache_dtype in SCALED else None
     pkv.paged_kv_append(kt, vt, torch.from_numpy(slots).cuda(), gk, gv, gks, gvs)
     torch.cuda.synchronize()
     oracle.ref_append(host, kt.float().cpu().numpy(), vt.float().cpu().numpy(), slots)
     assert np.array_equal(gpu_to_np_bits(gk).view(np.uint8), host.k.view(np.uint8))
     assert np.array_equal(gpu_to_np_bits(gv).view(np.uint8), host.v.view(np.uint8))
-    if cache_dtype == "i8":
+    if cache_dtype in SCALED:
         assert np.array_equal(gks.cpu().numpy().view(np.uint32), host.k_scales.view(np.uint32))
         assert np.array_equal(gvs.cpu().numpy().view(np.uint32), host.v_scales.view(np.uint32))
 
@@ -96,24 +96,27 @@ def test_append_full_size_bf16_and_out_of_pool_slots(pkv):
     assert np.array_equal(gpu_to_np_bits(gv), host.v)
 
 
-def test_append_full_size_int8(pkv):
-    w, _ = config_case("C5")
-    say("append C5 full size int8")
-    host = oracle.PagedCache(w.num_pages, w.num_kv_heads, w.head_dim, "i8")
+@pytest.mark.parametrize("name,dt", [("C5", "i8"), ("F1", "fp8")])
+def test_append_full_size_scaled(pkv, name, dt):
+    """Every token of the int8 (TinyLlama shape) and FP8 (Qwen2.5-1.5B shape)
+    decode workloads quantized in one call, codes and scales byte for byte."""
+    w, _ = config_case(name)
+    say(f"append {name} full size {dt}")
+    host = oracle.PagedCache(w.num_pages, w.num_kv_heads, w.head_dim, dt)
     gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
     gks, gvs = np_to_gpu(host.k_scales), np_to_gpu(host.v_scales)
     pkv.paged_kv_append(torch.from_numpy(w.k).cuda(), torch.from_numpy(w.v).cuda(),
                         torch.from_numpy(w.slot_mapping).cuda(), gk, gv, gks, gvs)
     torch.cuda.synchronize()
     oracle.ref_append(host, w.k, w.v, w.slot_mapping)
-    assert np.array_equal(gk.cpu().numpy(), host.k)
-    assert np.array_equal(gv.cpu().numpy(), host.v)
+    assert np.array_equal(gpu_to_np_bits(gk), host.k)
+    assert np.array_equal(gpu_to_np_bits(gv), host.v)
     assert np.array_equal(gks.cpu().numpy().view(np.uint32), host.k_scales.view(np.uint32))
     assert np.array_equal(gvs.cpu().numpy().view(np.uint32), host.v_scales.view(np.uint32))
 
 
 # ------------------------------------------------------------------ decode
-@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C5"])
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C5", "F1"])
 def test_decode_config_full_size(pkv, name):
     w, cache = config_case(name)
     say(f"decode {name} full size: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} kv={w.kv_dtype}")
@@ -122,7 +125,7 @@ def test_decode_config_full_size(pkv, name):
     assert err <= tol
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16", "f16", "i8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "f16", "i8", "fp8"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (9, 3), (8, 1), (32, 2)])
 def test_decode_small(pkv, kv, d, hq, hkv):
@@ -142,7 +145,7 @@ def test_decode_io_dtypes(pkv, q_dtype, out_dtype):
     assert err <= tol, err
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8", "fp8"])
 def test_decode_split_counts_agree(pkv, kv):
     """Raising max_context_len changes how contexts are split into
     partitions (and how many partials the LSE reduce merges); the result

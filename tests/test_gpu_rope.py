@@ -40,6 +40,9 @@ def _close(got: np.ndarray, want: np.ndarray, kind: str, what: str):
     """Within one ulp (one code for int8); returns the count not identical."""
     if kind == "i8":
         d = np.abs(got.astype(np.int64) - want.astype(np.int64))
+    elif kind == "fp8":                 # sign-magnitude codes -> ordered integers
+        o = lambda c: np.where(c & 0x80, -(c & 0x7F), c & 0x7F).astype(np.int64)  # noqa: E731
+        d = np.abs(o(got.astype(np.int64)) - o(want.astype(np.int64)))
     else:
         d = np.abs(_ordered(np.ascontiguousarray(got)) - _ordered(np.ascontiguousarray(want)))
     if d.max(initial=0) > 1:
@@ -59,7 +62,7 @@ def _case(T, hkv, hq, d, seed):
     return w, pos, q
 
 
-@pytest.mark.parametrize("cache_dtype", ["f32", "bf16", "f16", "i8"])
+@pytest.mark.parametrize("cache_dtype", ["f32", "bf16", "f16", "i8", "fp8"])
 @pytest.mark.parametrize("new_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16"), ("f16", "f32"),
                                                ("f32", "f16")])
 @pytest.mark.parametrize("d,style", [(64, "half"), (128, "half"), (64, "interleaved"),
@@ -79,11 +82,12 @@ def test_append_rope_matches_oracle(pkv, cache_dtype, new_dtype, q_dtype, d, sty
     slots = w.slot_mapping.copy()
     slots[[7, 100]] = -1
     host = oracle.PagedCache(w.num_pages, hkv, d, cache_dtype)
-    for arr in (host.k, host.v) + ((host.k_scales, host.v_scales) if cache_dtype == "i8" else ()):
+    scaled = cache_dtype in ("i8", "fp8")
+    for arr in (host.k, host.v) + ((host.k_scales, host.v_scales) if scaled else ()):
         arr.view(np.uint8)[:] = 0xA5
     gk, gv = np_to_gpu(host.k), np_to_gpu(host.v)
-    gks = np_to_gpu(host.k_scales) if cache_dtype == "i8" else None
-    gvs = np_to_gpu(host.v_scales) if cache_dtype == "i8" else None
+    gks = np_to_gpu(host.k_scales) if scaled else None
+    gvs = np_to_gpu(host.v_scales) if scaled else None
     pkv.paged_kv_append_rope(kt, vt, torch.from_numpy(slots).cuda(), torch.from_numpy(pos).cuda(),
                              gk, gv, theta, style, q=qt, k_scales=gks, v_scales=gvs)
     torch.cuda.synchronize()
@@ -103,7 +107,7 @@ def test_append_rope_matches_oracle(pkv, cache_dtype, new_dtype, q_dtype, d, sty
     assert np.array_equal(got_k[s0 // 16, :, s0 % 16].view(np.uint8),
                           host.k[s0 // 16, :, s0 % 16].view(np.uint8))
     n_off = _close(got_k, host.k, cache_dtype, "K")
-    if cache_dtype == "i8":
+    if scaled:
         assert np.array_equal(gvs.cpu().numpy().view(np.uint32), host.v_scales.view(np.uint32))
         n_off += _close(gks.cpu().numpy(), host.k_scales, "f32", "K scales")
     want_q = oracle.ref_rope_q(q_before, pos, theta, style, q_dtype)

@@ -45,7 +45,7 @@ def _decode(pkv, w, gc, q, bt, window, mcl=None):
     return out
 
 
-@pytest.mark.parametrize("kv,d", [("f32", 64), ("bf16", 128), ("f16", 64), ("i8", 128)])
+@pytest.mark.parametrize("kv,d", [("f32", 64), ("bf16", 128), ("f16", 64), ("i8", 128), ("fp8", 64)])
 @pytest.mark.parametrize("window", [1, 7, 16, 17, 32, 33, 100, 1000])
 def test_decode_window(pkv, kv, d, window):
     say(f"decode window={window} kv={kv} d={d}")

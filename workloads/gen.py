@@ -150,6 +150,14 @@ def _c2(seed):
                   meta={"desc": "paged decode, bf16 KV, Qwen2.5-1.5B shape, B=64, 12/2 heads, d=128"})
 
 
+def _f1(seed):
+    """The C2 draw (same seed, same values) stored as FP8 E4M3 codes."""
+    w = _c2(seed)
+    w.name, w.kv_dtype = "F1", "fp8"
+    w.meta = {"desc": "paged decode, FP8 E4M3 KV + per-token-head fp32 scales, Qwen2.5-1.5B shape, B=64, 12/2 heads, d=128"}
+    return w
+
+
 def _c3(seed):
     rng = np.random.Generator(np.random.PCG64(seed))
     ctx = rng.integers(64, 1024, size=384, endpoint=True)
@@ -227,7 +235,7 @@ def _w1(seed):
 
 
 CONFIGS = {"C1": (_c1, 1), "C2": (_c2, 2), "C3": (_c3, 3), "C4": (_c4, 4), "C5": (_c5, 5),
-           "W1": (_w1, 8)}
+           "W1": (_w1, 8), "F1": (_f1, 2)}
 
 
 def make_workload(name: str, seed: Optional[int] = None) -> Workload:
