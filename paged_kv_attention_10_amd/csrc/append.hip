@@ -6,7 +6,9 @@
 // page, table "Model architecture support", row "RoPE": every forward path,
 // configurable theta).
 //
-// Work split: a row is one head vector of one token (a K row, a V row, or
+// Work split.  Small plain appends (up to 4096 (token, KV head) rows, e.g.
+// a decode step) take one wave per (token, KV head).  Otherwise a row is one
+// head vector of one token (a K row, a V row, or
 // with RoPE a query row); a thread owns a 16-element segment of a row and
 // loads it with 16-byte loads, so a row of D elements takes D/16
 // consecutive lanes.  K/V workgroups take as many whole tokens as their 256
@@ -306,6 +308,80 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
   }
 }
 
+// Small appends (a decode step's new tokens): one wave per (token, KV head)
+// moves the token's K row and V row, each lane D/64 consecutive elements.
+// Its chain per token is short and its waves spread over many CUs, which
+// beats the segment kernel's LDS staging below a few thousand (token, head)
+// rows.  No RoPE (that path shares angle tables across a token's heads).
+template <int D>
+__device__ __forceinline__ void row_append(const AppendArgs& a, const void* src, void* cache,
+                                           float* scales, long row, long page, int off, int g,
+                                           bool is_v, int lane) {
+  constexpr int PER = D / 64;
+  float x[PER];
+  uint32_t raw[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const long i = row * D + lane * PER + e;
+    if (a.new_dtype == PKV_F32) {
+      raw[e] = static_cast<const uint32_t*>(src)[i];
+      x[e] = __uint_as_float(raw[e]);
+    } else {
+      x[e] = load_as_f32(src, i, a.new_dtype);
+      raw[e] = __float_as_uint(x[e]);
+    }
+  }
+  const long head = page * a.hkv + g;
+  auto dst_index = [&](int d) -> long {
+    return is_v ? (head * D + d) * kPage + off : (head * kPage + off) * D + d;
+  };
+  if (kv_scaled(a.cache_dtype)) {
+    float am = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) am = fmaxf(am, fabsf(x[e]));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) am = fmaxf(am, __shfl_xor(am, m));
+    const bool i8 = a.cache_dtype == PKV_I8;
+    const float sc = am / (i8 ? 127.0f : 448.0f);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      uint32_t code = 0u;
+      if (sc > 0.f) {
+        if (i8) code = (uint32_t)(int)fminf(fmaxf(rintf(x[e] / sc), -127.f), 127.f) & 0xffu;
+        else code = f32_to_e4m3_bits(fminf(fmaxf(x[e] / sc, -448.f), 448.f));
+      }
+      static_cast<uint8_t*>(cache)[dst_index(lane * PER + e)] = (uint8_t)code;
+    }
+    if (lane == 0) scales[head * kPage + off] = sc;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const long di = dst_index(lane * PER + e);
+    if (a.cache_dtype == PKV_F32) static_cast<uint32_t*>(cache)[di] = raw[e];
+    else static_cast<uint16_t*>(cache)[di] = (uint16_t)storage_bits(a.cache_dtype, x[e], raw[e]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kAppendThreads) void append_rows_kernel(AppendArgs a) {
+  const long w = (long)blockIdx.x * (kAppendThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= (long)a.num_tokens * a.hkv) return;
+  const long tok = w / a.hkv;
+  const int g = (int)(w - tok * a.hkv);
+  const int64_t slot = a.slots[tok];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const long page = slot / kPage;
+  const int off = (int)(slot - page * kPage);
+  const long row = tok * a.hkv + g;
+  row_append<D>(a, a.k_new, a.k_cache, a.k_scales, row, page, off, g, false, lane);
+  row_append<D>(a, a.v_new, a.v_cache, a.v_scales, row, page, off, g, true, lane);
+}
+
+// (token, KV head) rows up to which a plain append takes the row kernel.
+constexpr long kRowAppendMaxRows = 4096;
+
 // Consecutive workgroup ids go to different XCDs (and L2s); remap them so
 // that runs of consecutive K/V workgroups (neighbouring tokens, often one
 // page) share an XCD.
@@ -328,6 +404,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 
 // Shared checks and launch of both entry points.
 static int append_launch(AppendArgs& a, int head_dim, bool rope, pkv_stream_t stream) {
+  if (!rope && (long)a.num_tokens * a.hkv <= kRowAppendMaxRows) {
+    const long blocks = ((long)a.num_tokens * a.hkv + kAppendThreads / 64 - 1) / (kAppendThreads / 64);
+    clear_launch_error();
+    if (head_dim == 64)
+      hipLaunchKernelGGL(append_rows_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0,
+                         (hipStream_t)stream, a);
+    else
+      hipLaunchKernelGGL(append_rows_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0,
+                         (hipStream_t)stream, a);
+    return launch_status();
+  }
   const int nseg = head_dim / kSegElems;
   auto tokens_per_block = [](long segs) {
     long t = kAppendThreads / segs;

@@ -39,10 +39,13 @@ def _decode_check(pkv, w, cache, q_dtype="f32", out_dtype=torch.float32, tol=Non
 @pytest.mark.parametrize("cache_dtype", ["f32", "bf16", "f16", "i8", "fp8"])
 @pytest.mark.parametrize("new_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_append_bit_exact(pkv, cache_dtype, new_dtype, d):
-    say(f"append cache={cache_dtype} new={new_dtype} d={d}")
-    w = custom_workload(context_lens=[37, 16, 1, 90], num_q_heads=4, num_kv_heads=2, head_dim=d,
-                        kv_dtype=cache_dtype, num_pages=20, seed=40 + d)
+@pytest.mark.parametrize("lens", [[37, 16, 1, 90], [37, 16, 1, 90, 2100]], ids=["rows", "segments"])
+def test_append_bit_exact(pkv, cache_dtype, new_dtype, d, lens):
+    """A few (token, head) rows take the row kernel; past 4096 rows the
+    segment kernel with the LDS-transposed V stores."""
+    say(f"append cache={cache_dtype} new={new_dtype} d={d} tokens={sum(lens)}")
+    w = custom_workload(context_lens=lens, num_q_heads=4, num_kv_heads=2, head_dim=d,
+                        kv_dtype=cache_dtype, num_pages=(sum(lens) + 15) // 16 + 8, seed=40 + d)
     k, v = w.k.copy(), w.v.copy()
     # edge values: signed zeros, fp16 subnormals and overflow, bf16 ties, an all-zero vector
     k[0, 0, :8] = [0.0, -0.0, 2.0**-25, 3 * 2.0**-25, 6e-8, 65520.0, 1.00390625, -1.01171875]
@@ -57,6 +60,7 @@ def test_append_bit_exact(pkv, cache_dtype, new_dtype, d):
     vt = torch.from_numpy(v).cuda().to(TORCH_DT[new_dtype])
     slots = w.slot_mapping.copy()
     slots[[5, 40]] = -1
+    slots[41] = w.num_pages * 16 + 3          # past the pool: skipped like padding
     host = oracle.PagedCache(w.num_pages, 2, d, cache_dtype)
     host.k.view(np.uint8)[:] = 0xA5
     host.v.view(np.uint8)[:] = 0xA5
@@ -68,6 +72,7 @@ def test_append_bit_exact(pkv, cache_dtype, new_dtype, d):
     gvs = np_to_gpu(host.v_scales) if cache_dtype in SCALED else None
     pkv.paged_kv_append(kt, vt, torch.from_numpy(slots).cuda(), gk, gv, gks, gvs)
     torch.cuda.synchronize()
+    slots[41] = -1
     oracle.ref_append(host, kt.float().cpu().numpy(), vt.float().cpu().numpy(), slots)
     assert np.array_equal(gpu_to_np_bits(gk).view(np.uint8), host.k.view(np.uint8))
     assert np.array_equal(gpu_to_np_bits(gv).view(np.uint8), host.v.view(np.uint8))
