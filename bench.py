@@ -4,9 +4,11 @@
 Headline workload: paged decode with a bf16 KV cache at the Qwen2.5-1.5B
 attention shape (batch 64, 12 query / 2 KV heads, head_dim 128, 16-token
 pages, context lengths uniform in [512, 4096], pages scattered over a
-20k-page pool).  One step = append of the step's 64 new tokens + the decode
-call (the split-context partition kernel, then the log-sum-exp reduce
-kernel on the same stream when a context is split).  Before every
+20k-page pool).  One step = the step's 64 new tokens appended + the decode
+over every context, as one fused call (paged_attn_decode_append: the
+split-context partition kernel, which also stores the new tokens, then the
+log-sum-exp reduce kernel on the same stream when a context is split); the
+same step as two calls (append, then decode) is reported beside it.  Before every
 timed step a 1 GiB read evicts L2 and the 256 MB MALL, so every step reads
 its KV from HBM; each step is timed with HIP events on the stream the
 library launches on (the flush is outside the events).
@@ -179,6 +181,10 @@ def stats(xs):
 
 
 def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
+    """One step = the step's new tokens appended + the decode call.  With a
+    16- or 32-bit cache the step is one fused call (paged_attn_decode_append);
+    the same step as two calls (paged_kv_append, then paged_attn_decode) is
+    timed beside it.  int8/FP8 caches take the two calls."""
     from workloads import make_workload
     w = make_workload(name)
     log(f"[bench] {name}: building the pool on the GPU")
@@ -197,12 +203,17 @@ def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
     nws = g.pkv.paged_attn_decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads,
                                                   w.head_dim, w.max_context_len, window)
     ws = g.torch.zeros(max(nws, 16), dtype=g.torch.uint8, device=g.dev)
+    fused = w.kv_dtype in ("f32", "bf16", "f16")
 
     def decode():
         g.pkv.paged_attn_decode(q, k, v, bt, cl, w.max_context_len, w.scale, out=out,
                                 k_scales=ks, v_scales=vs, workspace=ws, window=window)
 
-    def step(inner, e1=None, e2=None):
+    def decode_step():
+        g.pkv.paged_attn_decode_append(q, k_new, v_new, k, v, bt, cl, w.max_context_len, w.scale,
+                                       out=out, workspace=ws, window=window)
+
+    def two_calls(inner, e1=None, e2=None):
         g.pkv.paged_kv_append(k_new, v_new, slots_new, k, v, ks, vs)
         if e1 is not None:
             e1.record()
@@ -210,13 +221,28 @@ def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
         if e2 is not None:
             e2.record()
 
+    def one_call(inner, e1=None, e2=None):
+        if e1 is not None:
+            e1.record()
+        inner()
+        if e2 is not None:
+            e2.record()
+
     log(f"[bench] {name}: {warmup} warmup + {steps} timed steps")
-    step_ms, inner_ms, wall = g.timed_steps(step, decode, steps, warmup)
+    if fused:
+        step_ms, inner_ms, wall = g.timed_steps(one_call, decode_step, steps, warmup)
+        two_ms, dec_ms, _ = g.timed_steps(two_calls, decode, steps, warmup)
+    else:
+        step_ms, inner_ms, wall = g.timed_steps(two_calls, decode, steps, warmup)
+        two_ms, dec_ms = step_ms, inner_ms
     nbytes = effective_kv_bytes(w)
-    st, si = stats(step_ms), stats(inner_ms)
+    st, si, sd = stats(step_ms), stats(inner_ms), stats(dec_ms)
     res = {
         "workload": name, "desc": DESC[name], "effective_kv_bytes": nbytes,
+        "step": ("paged_attn_decode_append (the new tokens appended and attended in one launch)"
+                 if fused else "paged_kv_append, then paged_attn_decode"),
         "ms_per_step": st["mean"], "step_ms": st, "decode_call_ms": si,
+        "two_call_step_ms": stats(two_ms), "decode_only_call_ms": sd,
         "kv_gbs": nbytes / (st["mean"] * 1e-3) / 1e9,
         "seq_tokens_per_s": w.batch / (st["mean"] * 1e-3),
         "context_tokens_per_s": float(w.context_lens.sum()) / (st["mean"] * 1e-3),
@@ -479,7 +505,7 @@ def main():
             "config": {"workload": DESC["C2"], "batch": 64, "num_q_heads": 12, "num_kv_heads": 2,
                        "head_dim": 128, "page_size": 16, "kv_dtype": "bf16",
                        "context_tokens": int(w2.context_lens.sum()),
-                       "step": "append of 64 new tokens + decode (partition kernel, then LSE reduce kernel)",
+                       "step": "64 new tokens appended + decode, one fused call (partition kernel with the append, then LSE reduce kernel)",
                        "timing": "HIP events per step on the library's stream; 1 GiB read-only flush before each step, outside the events"},
             "hbm_frac": round(head["hbm_frac_step"], 4),
             "seq_tokens_per_s": round(head["seq_tokens_per_s"], 1),
@@ -488,7 +514,7 @@ def main():
                          "frac": round(head["decode_call_gbs"] / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("decode_C2_counters.txt",
                                                      source_sha("decode.hip", "decode_body.h", "pkv_device.h", "pkv_host.h")),
-                         "kernel": "paged_attn_decode call: decode_partition_kernel<128,bf16> + decode_reduce_kernel<128>, events around both",
+                         "kernel": "paged_attn_decode_append call: decode_partition_kernel<128,bf16,fused> + decode_reduce_kernel<128>, events around both",
                          "algorithmic_bytes_per_launch": head["effective_kv_bytes"]},
             "detail_C2": head,
         })

@@ -212,6 +212,42 @@ int paged_attn_decode(const void* q, int q_dtype,
                       void* out, int out_dtype,
                       void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
+/*
+ * paged_attn_decode_append - one decode step in one launch: each sequence's
+ * new token is appended, then every sequence's query attends over its
+ * context including that token.
+ *
+ * The cached-decode step of the pages' runtimes (TinyLoop "Current Status",
+ * table "Core inference", row "Generation": the new token's K/V join the
+ * paged cache, then the query attends over it) with the append fused into
+ * the decode.  The result is exactly that of paged_kv_append of k_new/v_new
+ * to the slot of position context_lens[b] - 1 (page
+ * block_tables[b][(ctx-1)/16], offset (ctx-1)%16) followed by
+ * paged_attn_decode with the same arguments: the new row is stored with
+ * paged_kv_append's rounding and the attention uses the stored values.
+ *
+ *   k_new, v_new   [batch][num_kv_heads][head_dim], dtype new_dtype
+ *                  (F32/BF16/F16); read only.
+ *   k_cache, v_cache  written at the new tokens' slots, read elsewhere.
+ *   kv_dtype       PKV_F32, PKV_BF16 or PKV_F16 (int8 and FP8 quantise a
+ *                  whole row and return PKV_ERR_UNSUPPORTED here).
+ *   other arguments as for paged_attn_decode; the workspace size is
+ *                  paged_attn_decode_workspace_bytes(...).
+ *
+ * A sequence with context_lens[b] == 0 appends nothing and gets zeros.  A
+ * new token whose page id or context length is invalid is not stored (the
+ * row's output is NaN, as in paged_attn_decode).
+ */
+int paged_attn_decode_append(const void* q, int q_dtype,
+                             const void* k_new, const void* v_new, int new_dtype,
+                             void* k_cache, void* v_cache, int kv_dtype,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len,
+                             int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                             int page_size, int num_pages, float scale, int window,
+                             void* out, int out_dtype,
+                             void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
 /* Workspace bytes paged_attn_decode needs for these shapes (0 when the
  * contexts fit one partition, or for invalid shapes).  Pure host
  * arithmetic; touches no device. */

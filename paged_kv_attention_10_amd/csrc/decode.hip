@@ -43,17 +43,21 @@ namespace pkv {
 #define PKV_DECODE_MIN_WAVES 2
 #endif
 
-template <int D, int KV>
+template <int D, int KV, bool FUSE>
 __global__ __launch_bounds__(64 * kDecodeWaves, PKV_DECODE_MIN_WAVES) void decode_partition_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DecodeSmem<D>::total];
-  decode_partition_body<D, KV>(a, smem, blockIdx.x, blockIdx.y, blockIdx.z);
+  decode_partition_body<D, KV, FUSE>(a, smem, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 template <int D, int KV>
 static void launch_decode(const DecodeArgs& a, pkv_stream_t stream) {
   dim3 grid(a.nsplits, a.hkv * a.head_tiles, a.batch);
-  hipLaunchKernelGGL((decode_partition_kernel<D, KV>), grid, dim3(64 * kDecodeWaves), 0,
-                     (hipStream_t)stream, a);
+  if (kv_code8(KV) || !a.k_new)
+    hipLaunchKernelGGL((decode_partition_kernel<D, KV, false>), grid, dim3(64 * kDecodeWaves), 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<D, KV, !kv_code8(KV)>), grid, dim3(64 * kDecodeWaves),
+                       0, (hipStream_t)stream, a);
   if (a.nsplits > 1)
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.hq, a.batch), dim3(64), 0,
                        (hipStream_t)stream, a);
@@ -84,14 +88,16 @@ extern "C" size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, 
   return decode_workspace_layout(batch, num_q_heads, head_dim, p).total;
 }
 
-extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache,
-                                 const void* v_cache, const float* k_scales,
-                                 const float* v_scales, int kv_dtype,
-                                 const int32_t* block_tables, int max_blocks_per_seq,
-                                 const int32_t* context_lens, int max_context_len, int batch,
-                                 int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                                 int num_pages, float scale, int window, void* out, int out_dtype,
-                                 void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+// Checks and launch shared by paged_attn_decode and paged_attn_decode_append
+// (k_new null for the former).
+static int decode_call(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                       const float* k_scales, const float* v_scales, int kv_dtype,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* context_lens, int max_context_len, int batch,
+                       int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                       int num_pages, float scale, int window, void* out, int out_dtype,
+                       void* workspace, size_t workspace_bytes, const void* k_new,
+                       const void* v_new, int new_dtype, pkv_stream_t stream) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return PKV_ERR_INVALID_ARG;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
@@ -108,7 +114,8 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
     return PKV_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(block_tables) || !aligned16(context_lens) ||
-      (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)))
+      (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)) ||
+      (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
     return PKV_ERR_MISALIGNED;
 
   DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, window);
@@ -143,9 +150,46 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
   a.nsplits = p.nsplits;
   a.window = window;
   a.scale_log2 = scale * kLog2e;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_dtype = new_dtype;
+  a.k_store = const_cast<void*>(k_cache);
+  a.v_store = const_cast<void*>(v_cache);
 
   clear_launch_error();
   if (head_dim == 64) dispatch_kv<64>(kv_dtype, a, stream);
   else dispatch_kv<128>(kv_dtype, a, stream);
   return launch_status();
+}
+
+extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache,
+                                 const void* v_cache, const float* k_scales,
+                                 const float* v_scales, int kv_dtype,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len, int batch,
+                                 int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                                 int num_pages, float scale, int window, void* out, int out_dtype,
+                                 void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+  return decode_call(q, q_dtype, k_cache, v_cache, k_scales, v_scales, kv_dtype, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                     num_kv_heads, head_dim, page_size, num_pages, scale, window, out, out_dtype,
+                     workspace, workspace_bytes, nullptr, nullptr, PKV_F32, stream);
+}
+
+extern "C" int paged_attn_decode_append(const void* q, int q_dtype, const void* k_new,
+                                        const void* v_new, int new_dtype, void* k_cache,
+                                        void* v_cache, int kv_dtype, const int32_t* block_tables,
+                                        int max_blocks_per_seq, const int32_t* context_lens,
+                                        int max_context_len, int batch, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int page_size,
+                                        int num_pages, float scale, int window, void* out,
+                                        int out_dtype, void* workspace, size_t workspace_bytes,
+                                        pkv_stream_t stream) {
+  if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
+  if (!io_dtype_ok(new_dtype) || !kv_dtype_ok(kv_dtype)) return PKV_ERR_INVALID_ARG;
+  if (kv_scaled(kv_dtype)) return PKV_ERR_UNSUPPORTED;
+  return decode_call(q, q_dtype, k_cache, v_cache, nullptr, nullptr, kv_dtype, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                     num_kv_heads, head_dim, page_size, num_pages, scale, window, out, out_dtype,
+                     workspace, workspace_bytes, k_new, v_new, new_dtype, stream);
 }

@@ -30,6 +30,15 @@ struct DecodeArgs {
   int tiles_per_split, nsplits;
   int window;                 // sliding window in tokens, 0 = the whole context
   float scale_log2;
+  // Fused decode step (null k_new: none): each sequence's new K/V row
+  // [batch][hkv][D] in new_dtype is stored at position ctx - 1 (through the
+  // block table) and attended from registers; k_store/v_store are the
+  // writable cache pointers.
+  const void* k_new;
+  const void* v_new;
+  int new_dtype;
+  void* k_store;
+  void* v_store;
 };
 
 // First position a query at position ctx - 1 attends: ctx - window with a
@@ -119,6 +128,124 @@ __device__ __forceinline__ void load_tile(DecodeTile<D, KV>& t, const DecodeArgs
   }
 }
 
+// Fused decode step.  The new token's K row and V column, converted to the
+// cache's storage format, are stashed per wave in LDS (the merge area,
+// unused while tiles stream: 2 * D * ES bytes per wave, K as 16-byte
+// chunks (s, k-group), V by d) and patched into the tile holding position
+// ctx - 1 when it comes up.  In load_tile's lane layout, K row `tau` of the
+// tile is MFMA row half u of the lanes with tile_row_of_lane(r) + 4u == tau
+// (all four k-groups), and V column `tau` is element tau % 8 of the lanes of
+// k-group tau / 8, d = 16 * blk + r.
+__device__ __forceinline__ int tile_row_of_lane(int r) {
+  return (r < 8 ? 0 : 16) + 8 * ((r >> 2) & 1) + (r & 3);
+}
+
+// The new token's values this lane converts: K chunk `lane` (16 bytes of
+// storage, 16/ES elements) for lanes below D*ES/16, and V elements
+// d = lane + 64h.  Loaded as fp32 (exact for every input dtype; an fp32
+// value's bits are kept).
+template <int D>
+struct NewRaw {
+  float k[8];
+  float v[D / 64];
+};
+
+template <int D, int KV>
+__device__ __forceinline__ void load_new_token(NewRaw<D>& nr, const DecodeArgs& a, int b, int g,
+                                               int lane) {
+  constexpr int ES = (KV == PKV_F32) ? 4 : 2;
+  const long nrow = ((long)b * a.hkv + g) * D;
+  if (lane < D * ES / 16) {
+#pragma unroll
+    for (int e = 0; e < 16 / ES; ++e) nr.k[e] = load_as_f32(a.k_new, nrow + lane * (16 / ES) + e, a.new_dtype);
+  }
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) nr.v[h] = load_as_f32(a.v_new, nrow + lane + 64 * h, a.new_dtype);
+}
+
+// Converts the loaded new token into the wave's stash and, with `store`,
+// writes it to the cache slot (page, off), rounding as the append rounds.
+template <int D, int KV>
+__device__ __forceinline__ void stash_new_token(char* stash, const NewRaw<D>& nr,
+                                                const DecodeArgs& a, int g, long page, int off,
+                                                bool store, int lane) {
+  static_assert(!kv_code8(KV), "the fused step stores 16- and 32-bit caches");
+  constexpr int ES = (KV == PKV_F32) ? 4 : 2;
+  auto conv = [](float x) -> uint32_t {
+    if constexpr (KV == PKV_F32) return __float_as_uint(x);
+    else if constexpr (KV == PKV_BF16) return f32_to_bf16_bits(x);
+    else return f32_to_f16_bits(x);
+  };
+  if (lane < D * ES / 16) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (ES == 4) w[e] = conv(nr.k[e]);
+      else w[e] = conv(nr.k[2 * e]) | (conv(nr.k[2 * e + 1]) << 16);
+    }
+    *reinterpret_cast<u32x4*>(stash + 16 * lane) = w;
+    if (store) {
+      char* krow = static_cast<char*>(a.k_store) + ((page * a.hkv + g) * kPage + off) * (long)D * ES;
+      *reinterpret_cast<u32x4*>(krow + 16 * lane) = w;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    const int d = lane + 64 * h;
+    const uint32_t bits = conv(nr.v[h]);
+    if constexpr (ES == 4) reinterpret_cast<uint32_t*>(stash + D * ES)[d] = bits;
+    else reinterpret_cast<uint16_t*>(stash + D * ES)[d] = (uint16_t)bits;
+    if (store) {
+      const long vi = ((page * a.hkv + g) * (long)D + d) * kPage + off;
+      if constexpr (ES == 4) static_cast<uint32_t*>(a.v_store)[vi] = bits;
+      else static_cast<uint16_t*>(a.v_store)[vi] = (uint16_t)bits;
+    }
+  }
+}
+
+// Puts the stashed new token (tile position tau) into a loaded tile.  Every
+// register index is static (selects on the lane's role): a runtime index
+// into the tile's registers would move the tile to scratch memory.
+template <int D, int KV>
+__device__ __forceinline__ void patch_new_token(DecodeTile<D, KV>& t, const char* stash, int tau,
+                                                int lane) {
+  constexpr int ES = (KV == PKV_F32) ? 4 : 2;
+  constexpr int KL = DecodeTile<D, KV>::KL;
+  const int r = lane & 15, kg = lane >> 4;
+  const int base = tile_row_of_lane(r);
+  const bool k0 = tau == base, k1 = tau == base + 4;
+#pragma unroll
+  for (int s = 0; s < KL; ++s) {
+    const int d0 = (KV == PKV_F32) ? 16 * s + 4 * kg : 32 * s + 8 * kg;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(stash + d0 * ES);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t.k[0][s][e] = k0 ? w[e] : t.k[0][s][e];
+      t.k[1][s][e] = k1 ? w[e] : t.k[1][s][e];
+    }
+  }
+  const bool vl = kg == (tau >> 3);
+  const int e = tau & 7;
+#pragma unroll
+  for (int blk = 0; blk < D / 16; ++blk) {
+    const int d = 16 * blk + r;
+    if constexpr (KV == PKV_F32) {
+      const uint32_t nv = reinterpret_cast<const uint32_t*>(stash + D * ES)[d];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        t.v[blk][q >> 2][q & 3] = (vl && q == e) ? nv : t.v[blk][q >> 2][q & 3];
+    } else {
+      const uint32_t nv = reinterpret_cast<const uint16_t*>(stash + D * ES)[d];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = t.v[blk][0][q];
+        const uint32_t pw = (e & 1) ? ((w & 0x0000ffffu) | (nv << 16)) : ((w & 0xffff0000u) | nv);
+        t.v[blk][0][q] = (vl && q == (e >> 1)) ? pw : w;
+      }
+    }
+  }
+}
+
 // LDS of one partition workgroup: the wave merge (per wave and head its
 // output row, max and sum), the split's page ids and the bad-page flag.
 template <int D>
@@ -136,7 +263,7 @@ struct DecodeSmem {
 // DecodeSmem<D>::total bytes.  With a.cu_q_lens set (a mixed batch), only
 // sequences with a one-token chunk are processed, their query and output
 // rows being cu_q_lens[b].
-template <int D, int KV>
+template <int D, int KV, bool FUSE = false>
 __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char* smem, int split,
                                                       int gy, int b) {
   constexpr bool kF32 = (KV == PKV_F32);
@@ -232,12 +359,36 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   const int wp0 = 2 * wt0;                                   // its first page
   const int npw = max(0, min(npages - wp0, 2 * ntw));
   __syncthreads();   // the split's page ids are in LDS
-  int pid = 0;
+  const bool ctx_ok = !bad;
+  int pid = 0, pid_ok = 1;
   if (lane < npw) {
     // a page wholly before the window (the first tile's first page at most)
     // takes the window's first page instead; its keys are masked
     pid = s_pid[max(wp0 + lane, p_lo) - 2 * st0];
-    if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
+    if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; pid_ok = 0; }
+  }
+
+  // ---- fused decode step: the wave whose tiles hold position ctx - 1 takes
+  //      the new token from k_new / v_new (loaded now, ahead of its tiles),
+  //      stores it to the cache (the first head tile only) and patches it
+  //      into the tile it streams
+  constexpr bool kFusable = FUSE && !kv_code8(KV);
+  char* const stash = smem + SM::o + wave * 2 * D * ((KV == PKV_F32) ? 4 : 2);
+  int t_new = -1, tau_new = 0, page_new = 0;
+  bool store_new = false;
+  NewRaw<D> nr;
+  if constexpr (kFusable) {
+    if (ctx >= 1) {
+      const int tl = (ctx - 1) >> 5;
+      if (tl >= wt0 && tl < wt0 + ntw) {
+        t_new = tl - wt0;
+        tau_new = (ctx - 1) & 31;
+        const int pl = ((ctx - 1) >> 4) - wp0;                 // the new token's page, lane of pid
+        page_new = __builtin_amdgcn_readlane(pid, pl);
+        store_new = ctx_ok && __builtin_amdgcn_readlane(pid_ok, pl) != 0 && ht == 0;
+        load_new_token<D, KV>(nr, a, b, g, lane);
+      }
+    }
   }
 
   f32x4 acc[NBLK];
@@ -398,6 +549,13 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
       const int i = i0 + r;
       if (i < ntw) {
         if (i + R - 1 < ntw) issue(ring[(r + R - 1) % R], i + R - 1);
+        if constexpr (kFusable) {
+          // the new token converts just before the first tile computes: its
+          // loads went out ahead of that tile's, so the wait is the tile's own
+          if (i == 0 && t_new >= 0)
+            stash_new_token<D, KV>(stash, nr, a, g, page_new, tau_new & 15, store_new, lane);
+          if (i == t_new) patch_new_token<D, KV>(ring[r], stash, tau_new, lane);
+        }
         compute(ring[r], i);
       }
     }

@@ -156,6 +156,9 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   da.nsplits = p.nsplits;
   da.window = window;
   da.scale_log2 = scale * kLog2e;
+  da.k_new = da.v_new = nullptr;
+  da.new_dtype = PKV_F32;
+  da.k_store = da.v_store = nullptr;
 
   PrefillArgs pa;
   pa.q = q;

@@ -24,7 +24,7 @@ def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert set(names) == {
         "pkv_abi_version", "pkv_status_string", "paged_kv_append", "paged_kv_append_rope",
-        "paged_attn_decode",
+        "paged_attn_decode", "paged_attn_decode_append",
         "paged_attn_decode_workspace_bytes", "paged_attn_prefill_chunk",
         "paged_attn_prefill_workspace_bytes", "paged_attn_mixed", "paged_attn_mixed_workspace_bytes"}
     for n in names:
@@ -200,3 +200,23 @@ def test_append_rope_rejects(lib, over, code):
 
 def test_append_rope_zero_tokens_is_noop(lib):
     assert _append_rope(lib, T=0, k=None, v=None, slots=None, pos=None) == 0
+
+
+def _decode_append(lib, **over):
+    a = dict(q=FAKE, qd=0, kn=FAKE, vn=FAKE, nd=0, k=FAKE, v=FAKE, kvd=1, bt=FAKE, mb=8, cl=FAKE,
+             mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125, win=0, out=FAKE, od=0,
+             ws=FAKE, wsb=1 << 20, st=None)
+    a.update(over)
+    return lib.paged_attn_decode_append(*a.values())
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    ({"kn": None}, INVALID), ({"vn": None}, INVALID), ({"nd": 3}, INVALID), ({"q": None}, INVALID),
+    ({"kvd": 3}, UNSUPPORTED), ({"kvd": 4}, UNSUPPORTED), ({"kvd": 5}, INVALID),
+    ({"hq": 5}, INVALID), ({"win": -1}, INVALID), ({"d": 96}, UNSUPPORTED),
+    ({"kn": FAKE + 4}, MISALIGNED), ({"vn": FAKE + 2}, MISALIGNED),
+    ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "wsb": 1024, "mb": 256}, WS_SMALL),
+])
+def test_decode_append_rejects(lib, over, code):
+    assert _decode_append(lib, **over) == code
