@@ -247,6 +247,7 @@ def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
         "seq_tokens_per_s": w.batch / (st["mean"] * 1e-3),
         "context_tokens_per_s": float(w.context_lens.sum()) / (st["mean"] * 1e-3),
         "decode_call_gbs": nbytes / (si["mean"] * 1e-3) / 1e9,
+        "decode_only_call_gbs": nbytes / (sd["mean"] * 1e-3) / 1e9,
         "wall_s_timed_region": wall,
         "plan_workspace_bytes": int(nws),
     }
@@ -478,8 +479,9 @@ def main():
     for name in ("C3", "C5", "C1", "W1", "F1"):
         if name in only:
             _, r, _ = bench_decode(g, name, args.steps, args.warmup)
-            r["roofline"] = {"bound": "hbm", "achieved": r["decode_call_gbs"], "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": r["decode_call_gbs"] / HBM_PEAK_GBS,
+            # the plain decode call (partition + reduce kernels), as profiled
+            r["roofline"] = {"bound": "hbm", "achieved": r["decode_only_call_gbs"], "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": r["decode_only_call_gbs"] / HBM_PEAK_GBS,
                              "traffic": profiled_traffic(f"decode_{name}_counters.txt",
                                                          source_sha("decode.hip", "decode_body.h", "pkv_device.h", "pkv_host.h"))}
             extras[f"decode_{name}"] = r

@@ -130,3 +130,27 @@ def test_decode_step_full_size(pkv):
     s = w.slot_mapping[last]
     assert np.array_equal(gpu_to_np_bits(gc["k"])[s // 16, :, s % 16], cache.k[s // 16, :, s % 16])
     assert np.array_equal(gpu_to_np_bits(gc["v"])[s // 16, :, :, s % 16], cache.v[s // 16, :, :, s % 16])
+
+
+def test_decode_step_many_workgroups(pkv):
+    """A step whose decode needs many rounds of workgroups (the fp16 decode
+    workload at the Stories110M shape: 384 sequences x 12 KV heads) stores
+    the new tokens with a launch of its own before the decode; same results
+    as the two calls, bit for bit, and as the oracle."""
+    from workloads import make_workload
+    say("decode step C3 (many workgroups)")
+    w = make_workload("C3")
+    cache, gc, kn, vn, last = _setup(w, "f16", "f32")
+    gc2 = {k: (None if t is None else t.clone()) for k, t in gc.items()}
+    q = q_tensor(w, "f32")
+    out = _fused(pkv, w, gc, q, kn, vn)
+    pkv.paged_kv_append(kn, vn, torch.from_numpy(w.slot_mapping[last]).cuda(), gc2["k"], gc2["v"])
+    two = pkv.paged_attn_decode(q, gc2["k"], gc2["v"], np_to_gpu(w.block_tables),
+                                np_to_gpu(w.context_lens), w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
+    assert torch.equal(gc["k"].view(torch.uint8), gc2["k"].view(torch.uint8))
+    assert torch.equal(gc["v"].view(torch.uint8), gc2["v"].view(torch.uint8))
+    oracle.ref_append(cache, w.k[last], w.v[last], w.slot_mapping[last])
+    ref = oracle.ref_decode(q_exact_values(q), cache, w.block_tables, w.context_lens, w.scale, 12)
+    assert oracle.max_abs_err(to_f64(out), ref) <= 1e-2
