@@ -411,7 +411,9 @@ def bench_rope(g: Gpu, steps: int, warmup: int):
         "fused_call_ms": sf, "plain_append_call_ms": sp,
         "algorithmic_bytes": nbytes, "fused_gbs": gbs,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic("append_rope_R1_counters.txt",
+                                                 source_sha("append.hip", "pkv_device.h", "pkv_host.h"))},
     }
 
 

@@ -19,6 +19,15 @@
 // the XCDs' separate L2 caches, which an in-kernel merge would have to
 // write back and invalidate).
 //
+// Fused decode step (paged_attn_decode_append).  The wave whose tiles hold
+// position ctx - 1 loads the sequence's new K/V row with its first tiles,
+// converts it as the append rounds, stashes it in the workgroup's merge area
+// of LDS (free while tiles stream), stores it to the cache and patches it
+// into the tile it streams, so the attention sees exactly the stored values.
+// When the partition grid needs more than one round of workgroups, the
+// in-kernel V column stores measured slower than a launch of their own, and
+// append_step_kernel stores the rows before the plain decode instead.
+//
 // MFMA mapping (16x16 tiles, wave64).  Scores are computed transposed,
 // S^T = K * Q^T: A = K (row = token), B = Q^T (column = query head of the
 // group, padded to 16).  The output layout puts, in lane (c + 16*j), the
@@ -59,13 +68,13 @@ __global__ __launch_bounds__(256) void append_step_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   if (w >= (long)a.batch * a.hkv) return;
   const int b = (int)(w / a.hkv), g = (int)(w - (long)b * a.hkv);
+  NewRaw<D> nr;
+  load_new_token<D, KV>(nr, a, b, g, lane);   // independent of the slot: in flight meanwhile
   bool bad = false;
   const int ctx = checked_ctx(a.context_lens[b], a.max_context_len, a.max_blocks, bad);
   if (bad || ctx < 1) return;
   const int page = a.block_tables[(long)b * a.max_blocks + ((ctx - 1) >> 4)];
   if ((unsigned)page >= (unsigned)a.num_pages) return;
-  NewRaw<D> nr;
-  load_new_token<D, KV>(nr, a, b, g, lane);
   __shared__ __attribute__((aligned(16))) char stash[4][2 * D * 4];
   stash_new_token<D, KV>(stash[threadIdx.x >> 6], nr, a, g, page, (ctx - 1) & 15, true, lane);
 }
