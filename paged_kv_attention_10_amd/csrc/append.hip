@@ -67,29 +67,23 @@ struct AppendArgs {
 constexpr int kMaxTokensPerBlock = 16;
 constexpr int kVTileBytes = 8192;
 
-// Eight consecutive elements of a row starting at element `e0` (a multiple
-// of 8): values as fp32 (exact for every input dtype) and, for an fp32
-// input, the raw bit pattern (copied, not re-encoded).
-__device__ __forceinline__ void load8(const void* row, int dtype, int e0, float* x, uint32_t* raw) {
-  if (dtype == PKV_F32) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(row) + e0);
-    const u32x4 lo = p[0], hi = p[1];
+// Elements e0..e0+7 and e1..e1+7 of a row in a 16- or 32-bit dtype: their
+// values and storage bits (an fp32 input keeps its bits; a 16-bit one's
+// value bits as fp32).  Both 16- or 32-byte loads issue before either
+// converts.
+__device__ __forceinline__ void load8x2(const void* row, int dtype, int e0, int e1, float* x,
+                                        uint32_t* raw) {
+  with_io_dtype(dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    uint32_t b[16];
+    io_bits_vec<8, DT>(row, e0, b);
+    io_bits_vec<8, DT>(row, e1, b + 8);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      raw[j] = lo[j];
-      raw[4 + j] = hi[j];
+    for (int j = 0; j < 16; ++j) {
+      x[j] = io_value<DT>(b[j]);
+      raw[j] = DT == PKV_F32 ? b[j] : __float_as_uint(x[j]);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = __uint_as_float(raw[j]);
-  } else {
-    const u32x4 h = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + e0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t b = (h[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-      x[j] = dtype == PKV_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
-      raw[j] = __float_as_uint(x[j]);
-    }
-  }
+  });
 }
 
 // Storage bits of one element in a 16- or 32-bit dtype.
@@ -170,8 +164,7 @@ __device__ void query_block(const AppendArgs& a, long qb, double2* cs) {
     char* row = static_cast<char*>(a.q) + (tok * a.hq + h) * D * es;
     float x[16];
     uint32_t raw[16];
-    load8(row, a.q_dtype, c0, x, raw);
-    load8(row, a.q_dtype, c1, x + 8, raw + 8);
+    load8x2(row, a.q_dtype, c0, c1, x, raw);
     rotate16(x, raw, cs + lt * (D / 2) + 8 * s, split);
     store8(row, a.q_dtype, c0, x, raw);
     store8(row, a.q_dtype, c1, x + 8, raw + 8);
@@ -223,8 +216,7 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
                       (tok * a.hkv + h) * D * (a.new_dtype == PKV_F32 ? 4 : 2);
     float x[16];
     uint32_t raw[16];
-    load8(src, a.new_dtype, c0, x, raw);
-    load8(src, a.new_dtype, c1, x + 8, raw + 8);
+    load8x2(src, a.new_dtype, c0, c1, x, raw);
     if (rotate) rotate16(x, raw, cs + lt * (D / 2) + 8 * s, split);
 
     const long head = page * a.hkv + h;
@@ -320,17 +312,17 @@ __device__ __forceinline__ void row_append(const AppendArgs& a, const void* src,
   constexpr int PER = D / 64;
   float x[PER];
   uint32_t raw[PER];
+  with_io_dtype(a.new_dtype, [&](auto ndt) {
+    constexpr int NT = decltype(ndt)::value;
+    uint32_t bits[PER];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const long i = row * D + lane * PER + e;
-    if (a.new_dtype == PKV_F32) {
-      raw[e] = static_cast<const uint32_t*>(src)[i];
-      x[e] = __uint_as_float(raw[e]);
-    } else {
-      x[e] = load_as_f32(src, i, a.new_dtype);
-      raw[e] = __float_as_uint(x[e]);
+    for (int e = 0; e < PER; ++e) bits[e] = io_bits<NT>(src, row * D + lane * PER + e);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      x[e] = io_value<NT>(bits[e]);
+      raw[e] = NT == PKV_F32 ? bits[e] : __float_as_uint(x[e]);
     }
-  }
+  });
   const long head = page * a.hkv + g;
   auto dst_index = [&](int d) -> long {
     return is_v ? (head * D + d) * kPage + off : (head * kPage + off) * D + d;

@@ -154,13 +154,20 @@ template <int D, int KV>
 __device__ __forceinline__ void load_new_token(NewRaw<D>& nr, const DecodeArgs& a, int b, int g,
                                                int lane) {
   constexpr int ES = (KV == PKV_F32) ? 4 : 2;
+  constexpr int KE = 16 / ES;                       // K elements per chunk
   const long nrow = ((long)b * a.hkv + g) * D;
-  if (lane < D * ES / 16) {
+  const int kc = lane < D * ES / 16 ? lane : 0;     // lanes past the chunks reload chunk 0
+  with_io_dtype(a.new_dtype, [&](auto ndt) {
+    constexpr int NT = decltype(ndt)::value;
+    uint32_t kb[KE], vb[D / 64];
+    io_bits_vec<KE, NT>(a.k_new, nrow + kc * KE, kb);
 #pragma unroll
-    for (int e = 0; e < 16 / ES; ++e) nr.k[e] = load_as_f32(a.k_new, nrow + lane * (16 / ES) + e, a.new_dtype);
-  }
+    for (int h = 0; h < D / 64; ++h) vb[h] = io_bits<NT>(a.v_new, nrow + lane + 64 * h);
 #pragma unroll
-  for (int h = 0; h < D / 64; ++h) nr.v[h] = load_as_f32(a.v_new, nrow + lane + 64 * h, a.new_dtype);
+    for (int e = 0; e < KE; ++e) nr.k[e] = io_value<NT>(kb[e]);
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) nr.v[h] = io_value<NT>(vb[h]);
+  });
 }
 
 // Converts the loaded new token into the wave's stash and, with `store`,
@@ -293,13 +300,29 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   // ---- one round trip for the context length, the query and the page ids
   //      of the whole split (loaded before the context length says which of
   //      them the split uses and how its tiles divide over the waves; entries
-  //      past the context are never used).  With a sliding window the split's
-  //      pages follow from the window start, so the context length comes
-  //      first and entries of pages wholly before the window are not read.
+  //      past the context are never used).  The query's loads go out first
+  //      and convert only after the page ids are in LDS: the page ids' wait
+  //      then covers both.  With a sliding window the split's pages follow
+  //      from the window start, so the context length comes first and
+  //      entries of pages wholly before the window are not read.
   const int raw_ctx = a.context_lens[b];
   bool bad = a.cu_q_lens && raw_ctx < 1;   // a chunk of one needs a context of at least one
   using SM = DecodeSmem<D>;
   int* const s_pid = reinterpret_cast<int*>(smem + SM::pid);
+
+  // the query's raw words (decoded below); columns past the group's heads
+  // load the group's first row and are zeroed when decoded
+  const bool q_live = c < nh;
+  const long qrow = ((long)qb * a.hq + h0 + (q_live ? c : 0)) * D;
+  constexpr int QRUN = kF32 ? 4 : 8;                 // elements per run
+  uint32_t qw[NSTEP / (kF32 ? 4 : 1)][QRUN];
+#pragma unroll
+  for (int r = 0; r < NSTEP / (kF32 ? 4 : 1); ++r) {
+    // fp32 KV: qf[4r + e] holds d = 16r + 4j + e; else run r starts at d0
+    const int d0 = kF32 ? 16 * r + 4 * j : (kI8 ? (64 * (r >> 1) + 16 * j + 8 * (r & 1)) : (32 * r + 8 * j));
+    io_words_rt<QRUN>(a.q, qrow + d0, a.q_dtype, qw[r]);
+  }
+
   int lo = 0, t_lo = 0;                    // window start and its tile
   if (a.window > 0) {
     bool dummy = false;
@@ -315,31 +338,25 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 
   float qf[kF32 ? NSTEP : 1];
   H8 qhi[kF32 ? 1 : NSTEP], qlo[kF32 ? 1 : NSTEP];
-  {
-    const long qrow = ((long)qb * a.hq + h0 + c) * D;
-    const bool live = c < nh;
-    if constexpr (kF32) {
+  if constexpr (kF32) {
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        int d = 16 * (s >> 2) + 4 * j + (s & 3);
-        qf[s] = live ? load_as_f32(a.q, qrow + d, a.q_dtype) : 0.f;
-      }
-    } else {
+    for (int s = 0; s < NSTEP; ++s)
+      qf[s] = q_live ? io_value_sel(io_word_bits(qw[s >> 2], s & 3, a.q_dtype), a.q_dtype) : 0.f;
+  } else {
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        int d0 = kI8 ? (64 * (s >> 1) + 16 * j + 8 * (s & 1)) : (32 * s + 8 * j);
-        float x[8];
+    for (int s = 0; s < NSTEP; ++s) {
+      float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? load_as_f32(a.q, qrow + d0 + e, a.q_dtype) : 0.f;
-        if constexpr (kBF16) {
-          auto sp = split_bf16(x);
-          qhi[s] = sp.hi;
-          qlo[s] = sp.lo;
-        } else {
-          auto sp = split_f16(x);
-          qhi[s] = sp.hi;
-          qlo[s] = sp.lo;
-        }
+      for (int e = 0; e < 8; ++e)
+        x[e] = q_live ? io_value_sel(io_word_bits(qw[s], e, a.q_dtype), a.q_dtype) : 0.f;
+      if constexpr (kBF16) {
+        auto sp = split_bf16(x);
+        qhi[s] = sp.hi;
+        qlo[s] = sp.lo;
+      } else {
+        auto sp = split_f16(x);
+        qhi[s] = sp.hi;
+        qlo[s] = sp.lo;
       }
     }
   }

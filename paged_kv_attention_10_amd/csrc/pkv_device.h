@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/pkv.h"
 
 namespace pkv {
@@ -42,11 +44,109 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// Load element i of a row in dtype dt as float.
-__device__ __forceinline__ float load_as_f32(const void* base, long i, int dt) {
-  if (dt == PKV_F32) return static_cast<const float*>(base)[i];
-  if (dt == PKV_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
-  return f16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+// ------------------------------------------------- inputs in an io dtype
+// Inputs come in fp32, bf16 or fp16, chosen at run time.  Code that loads
+// several elements runs under with_io_dtype, which branches once on the
+// dtype and hands the body the dtype as a compile-time constant: the loads
+// then issue back to back and are converted after one wait (a per-element
+// dtype branch makes each load wait inside its branch).
+template <int DT>
+using IoDtype = std::integral_constant<int, DT>;
+
+template <typename F>
+__device__ __forceinline__ void with_io_dtype(int dt, F&& body) {
+  if (dt == PKV_F32) body(IoDtype<PKV_F32>{});
+  else if (dt == PKV_BF16) body(IoDtype<PKV_BF16>{});
+  else body(IoDtype<PKV_F16>{});
+}
+
+// Storage bits of element i (16-bit values zero-extended) and their value.
+template <int DT>
+__device__ __forceinline__ uint32_t io_bits(const void* base, long i) {
+  if constexpr (DT == PKV_F32) return static_cast<const uint32_t*>(base)[i];
+  else return static_cast<const uint16_t*>(base)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ float io_value(uint32_t bits) {
+  if constexpr (DT == PKV_F32) return __uint_as_float(bits);
+  else if constexpr (DT == PKV_BF16) return bf16_bits_to_f32(bits);
+  else return f16_bits_to_f32(bits);
+}
+
+// The value of storage bits in the run-time dtype dt, with selects rather
+// than a branch: code that loads under with_io_dtype and converts later
+// keeps the conversion (and the wait for the loads) where it is written,
+// since a second branch on dt would be merged with the first.
+__device__ __forceinline__ float io_value_sel(uint32_t bits, int dt) {
+  const float vh = f16_bits_to_f32(bits);
+  const float vb = __uint_as_float(bits << 16);
+  return dt == PKV_F32 ? __uint_as_float(bits) : (dt == PKV_BF16 ? vb : vh);
+}
+
+// Raw words of N (4 or 8) consecutive elements i..: N words in fp32, N/2 in
+// a 16-bit dtype (element e in the low (e even) or high half of word e/2),
+// with 8-, 16- or 32-byte loads (base + i must be aligned to the load's
+// size).  Nothing here uses the loaded data.
+template <int N, int DT>
+__device__ __forceinline__ void io_words(const void* base, long i, uint32_t* w) {
+  static_assert(N == 4 || N == 8, "4 or 8 elements");
+  if constexpr (DT == PKV_F32) {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(base) + i + 4 * k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[4 * k + e] = v[e];
+    }
+  } else if constexpr (N == 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = v[e];
+  } else {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i);
+    w[0] = v[0];
+    w[1] = v[1];
+  }
+}
+
+// The same raw words for the run-time dtype dt, without a branch: two
+// 16-byte (N = 8) or 8-byte (N = 4) loads, the second repeating the first
+// in a 16-bit dtype (whose run fills only the first half of w).
+template <int N>
+__device__ __forceinline__ void io_words_rt(const void* base, long i, int dt, uint32_t* w) {
+  static_assert(N == 4 || N == 8, "4 or 8 elements");
+  const bool f32 = dt == PKV_F32;
+  const char* p = static_cast<const char*>(base) + i * (f32 ? 4 : 2);
+  if constexpr (N == 8) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + (f32 ? 16 : 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[e] = lo[e];
+      w[4 + e] = hi[e];
+    }
+  } else {
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + (f32 ? 8 : 0));
+    w[0] = lo[0];
+    w[1] = lo[1];
+    w[2] = hi[0];
+    w[3] = hi[1];
+  }
+}
+
+// Storage bits of element e of such words, for the run-time dtype dt.
+__device__ __forceinline__ uint32_t io_word_bits(const uint32_t* w, int e, int dt) {
+  return dt == PKV_F32 ? w[e] : (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+}
+
+// N consecutive elements i.. as storage bits (16-bit values zero-extended).
+template <int N, int DT>
+__device__ __forceinline__ void io_bits_vec(const void* base, long i, uint32_t* bits) {
+  uint32_t w[N];
+  io_words<N, DT>(base, i, w);
+#pragma unroll
+  for (int e = 0; e < N; ++e) bits[e] = io_word_bits(w, e, DT);
 }
 
 __device__ __forceinline__ void store_from_f32(void* base, long i, int dt, float x) {

@@ -123,27 +123,37 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
 
   // ---- Q^T fragments (B operand): column col, k-chunk d = 16*s + 8*hh
   H8 qhi[NSTEP], qlo[QSPLIT ? NSTEP : 1];
+  if constexpr (!QSPLIT) {
 #pragma unroll
-  for (int s = 0; s < NSTEP; ++s) {
-    const int d0 = 16 * s + 8 * hh;
-    if constexpr (!QSPLIT) {
+    for (int s = 0; s < NSTEP; ++s) {
+      const int d0 = 16 * s + 8 * hh;
       u32x4 w = live ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + qrow + d0)
                      : u32x4{0u, 0u, 0u, 0u};
       qhi[s] = __builtin_bit_cast(H8, w);
-    } else {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = live ? load_as_f32(a.q, qrow + d0 + e, a.q_dtype) : 0.f;
-      if constexpr (kBF16) {
-        auto sp = split_bf16(x);
-        qhi[s] = sp.hi;
-        qlo[s] = sp.lo;
-      } else {
-        auto sp = split_f16(x);
-        qhi[s] = sp.hi;
-        qlo[s] = sp.lo;
-      }
     }
+  } else {
+    // a dead row's qrow is the chunk's first row (valid): loaded, then zeroed
+    with_io_dtype(a.q_dtype, [&](auto qdt) {
+      constexpr int QT = decltype(qdt)::value;
+      uint32_t bits[NSTEP][8];
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) io_bits_vec<8, QT>(a.q, qrow + 16 * s + 8 * hh, bits[s]);
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? io_value<QT>(bits[s][e]) : 0.f;
+        if constexpr (kBF16) {
+          auto sp = split_bf16(x);
+          qhi[s] = sp.hi;
+          qlo[s] = sp.lo;
+        } else {
+          auto sp = split_f16(x);
+          qhi[s] = sp.hi;
+          qlo[s] = sp.lo;
+        }
+      }
+    });
   }
 
   // ---- page ids: a window of 64 consecutive entries of the block-table row,

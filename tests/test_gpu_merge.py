@@ -1,0 +1,97 @@
+"""GPU tests of the split merge: decodes whose contexts need several splits
+write per-split partials and log2-sum-exps to the workspace, merged by the
+reduce kernel.  One workspace serves calls of any shape, a bad page id in
+one split poisons only its sequence, and a large batch with a few long
+contexts splits only those."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (TOL, np_to_gpu, oracle_cache, poisoned_gpu_cache, q_exact_values, q_tensor,
+                         say, small_decode, to_f64, used_slot_mask)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_attention_10_amd as lib
+    return lib
+
+
+def _decode(pkv, w, gc, q, ws, window, block_tables=None):
+    bt = w.block_tables if block_tables is None else block_tables
+    out = pkv.paged_attn_decode(q, gc["k"], gc["v"], np_to_gpu(bt), np_to_gpu(w.context_lens),
+                                w.max_context_len, w.scale, k_scales=gc["ks"], v_scales=gc["vs"],
+                                workspace=ws, window=window)
+    torch.cuda.synchronize()
+    return out
+
+
+def _case(ctx, hq, hkv, d, kv, seed):
+    w = small_decode(ctx, hq, hkv, d, kv, seed=seed)
+    c = oracle_cache(w)
+    return w, c, poisoned_gpu_cache(c, used_slot_mask(w)), q_tensor(w, "f32")
+
+
+def _ws_bytes(pkv, w, window):
+    return pkv.paged_attn_decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads,
+                                                 w.head_dim, w.max_context_len, window)
+
+
+def test_one_workspace_across_shapes(pkv):
+    """Calls of three shapes (6 heads per group, two head tiles of a 20-head
+    group, fp32 with a window), every one split, take turns on one
+    workspace, twice over: each gives the bits of the same call on a fresh
+    workspace and the oracle's values."""
+    shapes = [([3000, 17, 4096, 1200, 2500, 64, 3900, 800], 12, 2, 128, "bf16", 0),
+              ([4096, 4000, 3001, 100], 40, 2, 64, "f16", 0),
+              ([5000, 300, 9000], 8, 8, 128, "f32", 700)]
+    cases = [(_case(ctx, hq, hkv, d, kv, 800 + i), win)
+             for i, (ctx, hq, hkv, d, kv, win) in enumerate(shapes)]
+    sizes = [_ws_bytes(pkv, w, win) for (w, _, _, _), win in cases]
+    assert min(sizes) > 0                          # every shape splits
+    ws = torch.full((max(sizes),), 0x7F, dtype=torch.uint8, device="cuda")
+    for rnd in range(2):
+        for (w, c, gc, q), win in cases:
+            say(f"shared workspace: round {rnd} batch={w.batch} hq={w.num_q_heads} "
+                f"hkv={w.num_kv_heads} d={w.head_dim} kv={w.kv_dtype} window={win}")
+            out = _decode(pkv, w, gc, q, ws, win)
+            again = _decode(pkv, w, gc, q, torch.empty_like(ws), win)
+            assert torch.equal(out, again)
+            ref = oracle.ref_decode(q_exact_values(q), c, w.block_tables, w.context_lens, w.scale,
+                                    w.num_q_heads, window=win)
+            assert oracle.max_abs_err(to_f64(out), ref) <= TOL[w.kv_dtype]
+
+
+def test_large_batch_with_few_split_contexts(pkv):
+    """4202 sequences x 4 KV heads: one split per sequence covers 4096
+    tokens, so only the two longer contexts are split and merged."""
+    ctx = [5000, 4500] + [1 + i % 8 for i in range(4200)]
+    say("large batch: 4202 sequences, hkv 4, d 64, bf16")
+    w, c, gc, q = _case(ctx, 4, 4, 64, "bf16", 820)
+    nws = _ws_bytes(pkv, w, 0)
+    assert nws > 0
+    out = _decode(pkv, w, gc, q, torch.empty(nws, dtype=torch.uint8, device="cuda"), 0)
+    ref = oracle.ref_decode(q_exact_values(q), c, w.block_tables, w.context_lens, w.scale, 4)
+    assert oracle.max_abs_err(to_f64(out), ref) <= TOL["bf16"]
+
+
+def test_merge_propagates_nan(pkv):
+    """A bad page id in one split of a split context makes that sequence's
+    rows NaN through the merge; the other sequences keep the oracle's
+    values."""
+    w, c, gc, q = _case([3000, 2900, 2000, 4096], 12, 2, 128, "bf16", 830)
+    bt = w.block_tables.copy()
+    bt[1, 5] = w.num_pages + 3
+    nws = _ws_bytes(pkv, w, 0)
+    out = _decode(pkv, w, gc, q, torch.empty(nws, dtype=torch.uint8, device="cuda"), 0,
+                  block_tables=bt)
+    o = out.cpu().numpy()
+    assert np.all(np.isnan(o[1])) and np.all(np.isfinite(o[[0, 2, 3]]))
+    ref = oracle.ref_decode(q_exact_values(q), c, w.block_tables, w.context_lens, w.scale, 12)
+    keep = [0, 2, 3]
+    assert oracle.max_abs_err(to_f64(out)[keep], ref[keep]) <= TOL["bf16"]
