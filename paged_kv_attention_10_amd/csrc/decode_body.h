@@ -76,9 +76,6 @@ struct DecodeTile {
 // query fragments and the accumulators stay within the VGPR budget.
 template <int D, int KV>
 constexpr int ring_depth() {
-#ifdef PKV_DECODE_RING
-  if (!(KV == PKV_F32 && D == 128)) return PKV_DECODE_RING;
-#endif
   return (KV == PKV_F32 && D == 128) ? 1 : 2;
 }
 
@@ -555,26 +552,49 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
     }
   };
 
-  // ---- stream the wave's tiles through the register ring
+  // ---- stream the wave's tiles through the register ring.  The loop body
+  //      holds no conditional loads or stores: the wait before a tile
+  //      computes then covers only that tile's loads, not the next tile's
+  //      issued just before (a load skipped on some path makes the wait
+  //      count for every path the worst one).  Tiles go in pairs; the one
+  //      load past the run's end reloads its last tile (from L2) and is
+  //      never computed.
   DecodeTile<D, KV> ring[R];
-#pragma unroll
-  for (int r = 0; r < R - 1; ++r)
-    if (r < ntw) issue(ring[r], r);
-  for (int i0 = 0; i0 < ntw; i0 += R) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = i0 + r;
-      if (i < ntw) {
-        if (i + R - 1 < ntw) issue(ring[(r + R - 1) % R], i + R - 1);
-        if constexpr (kFusable) {
-          // the new token converts just before the first tile computes: its
-          // loads went out ahead of that tile's, so the wait is the tile's own
-          if (i == 0 && t_new >= 0)
-            stash_new_token<D, KV>(stash, nr, a, g, page_new, tau_new & 15, store_new, lane);
-          if (i == t_new) patch_new_token<D, KV>(ring[r], stash, tau_new, lane);
-        }
-        compute(ring[r], i);
+  if constexpr (R == 1) {
+    for (int i = 0; i < ntw; ++i) {
+      issue(ring[0], i);
+      if constexpr (kFusable) {
+        if (i == 0 && t_new >= 0)
+          stash_new_token<D, KV>(stash, nr, a, g, page_new, tau_new & 15, store_new, lane);
+        if (i == t_new) patch_new_token<D, KV>(ring[0], stash, tau_new, lane);
       }
+      compute(ring[0], i);
+    }
+  } else {
+    static_assert(R == 2, "a ring of one or two tiles");
+    if (ntw > 0) issue(ring[0], 0);
+    if constexpr (kFusable) {
+      // the new token's loads went out ahead of the first tile's, so this
+      // waits only for them
+      if (t_new >= 0) stash_new_token<D, KV>(stash, nr, a, g, page_new, tau_new & 15, store_new, lane);
+    }
+    for (int i = 0; i + 1 < ntw; i += 2) {
+      issue(ring[1], i + 1);
+      if constexpr (kFusable) {
+        if (i == t_new) patch_new_token<D, KV>(ring[0], stash, tau_new, lane);
+      }
+      compute(ring[0], i);
+      issue(ring[0], min(i + 2, ntw - 1));
+      if constexpr (kFusable) {
+        if (i + 1 == t_new) patch_new_token<D, KV>(ring[1], stash, tau_new, lane);
+      }
+      compute(ring[1], i + 1);
+    }
+    if (ntw & 1) {
+      if constexpr (kFusable) {
+        if (ntw - 1 == t_new) patch_new_token<D, KV>(ring[0], stash, tau_new, lane);
+      }
+      compute(ring[0], ntw - 1);
     }
   }
   const float l_run = wave_sum_xor_16_32(l_part);
