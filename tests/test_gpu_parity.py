@@ -220,6 +220,48 @@ def test_prefill_config_full_size(pkv):
     assert err <= 1e-2
 
 
+@pytest.mark.parametrize("case", ["spread_many_blocks", "spread_few_blocks", "uniform", "batch_over_256"])
+def test_prefill_row_block_order(pkv, case):
+    """Every row block is computed exactly once whichever order the workgroups
+    take them in: contexts that differ (ranked order, with more and with fewer
+    row blocks than the first round of 256 workgroups), contexts within 25% of
+    each other (grid order) and more than 256 sequences (grid order).  The
+    output starts as NaN, so a row no workgroup wrote fails."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    if case == "spread_many_blocks":       # 12 sequences x 2 KV heads x 12 row blocks = 288 > 256
+        ql = [256] * 12
+        pre = rng.integers(0, 1200, size=12).tolist()
+        hq, hkv = 12, 2
+    elif case == "spread_few_blocks":
+        ql = [40, 90, 7, 130]
+        pre = [900, 0, 333, 61]
+        hq, hkv = 6, 2
+    elif case == "uniform":
+        ql = [128] * 10
+        pre = [500 + 10 * i for i in range(10)]
+        hq, hkv = 6, 2
+    else:
+        ql = rng.integers(1, 6, size=300).tolist()
+        pre = rng.integers(0, 120, size=300).tolist()
+        hq, hkv = 4, 2
+    ctx = [p + c for p, c in zip(pre, ql)]
+    w = small_prefill(ctx, ql, hq, hkv, 64, "bf16", seed=len(ctx))
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w, "bf16")
+    out = torch.full((int(w.cu_q_lens[-1]), hq, 64), float("nan"), device="cuda")
+    say(f"prefill row-block order: {case}, batch {len(ctx)}")
+    pkv.paged_attn_prefill_chunk(q, gc["k"], gc["v"], np_to_gpu(w.block_tables),
+                                 np_to_gpu(w.context_lens), np_to_gpu(w.cu_q_lens), w.max_q_len,
+                                 w.max_context_len, w.scale, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.ref_prefill_chunk(q_exact_values(q), cache, w.block_tables, w.context_lens,
+                                   w.cu_q_lens, w.scale)
+    got = to_f64(out)
+    assert not np.isnan(got).any()
+    assert oracle.max_abs_err(got, ref) <= 1e-2
+
+
 @pytest.mark.parametrize("kv", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (6, 2), (12, 2), (3, 1)])
