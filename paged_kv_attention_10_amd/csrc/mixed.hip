@@ -6,8 +6,11 @@
 // P_b + i and attends to [0, P_b + i]; a decode token is a chunk of one.
 //
 // One launch holds two kinds of workgroups.  The first part of the grid is
-// the prefill kernel's row blocks (heaviest first); sequences whose chunk is
-// a single token leave them empty.  The second part is the decode kernel's
+// the prefill kernel's row blocks in grid order (heaviest first); sequences
+// whose chunk is a single token leave them empty, and such a workgroup
+// exits after one load (ranking the sequences first, as the prefill kernel
+// may, measured slower here: every empty workgroup pays for the ranking
+// before the decode partitions behind it can start).  The second part is the decode kernel's
 // partitions, which take exactly those single-token sequences (their query
 // and output rows mapped through cu_q_lens): a decode token is walked by
 // four waves with 16-query-head MFMA tiles instead of occupying a 128-row

@@ -44,60 +44,14 @@
 
 namespace pkv {
 
-// Which row block a workgroup takes.  Workgroup ids are dealt round robin
-// to the XCDs and, within one, to its CUs in turn, and two workgroups share
-// a CU; a row block's time grows with its sequence's context.  With at most
-// kPrefillSortMaxBatch sequences every workgroup ranks the sequences by
-// context length (ties by index) from the same loads, so all agree on one
-// permutation: the first kPrefillFirstRound ids (one per CU of a 256-CU
-// MI355X) take the heaviest row blocks, and the later ids the rest lightest
-// first, so that a CU's second workgroup tends to be a light one and every
-// XCD gets a share of the long sequences.  That spreads each sequence's K/V
-// over all XCDs' L2s, so it pays only when the contexts differ: when the
-// longest is within 25% of the shortest, and for larger batches, the grid
-// order stays (each sequence's row blocks on one XCD, heavier ones first).
-constexpr int kPrefillSortMaxBatch = 256;
-constexpr long kPrefillFirstRound = 256;
-
-// Returns false (and leaves b, g, rb alone) when the grid order is kept.
-__device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int* sh, int& b, int& g,
-                                             int& rb) {
-  const int B = a.batch, H = a.hkv, R = a.nrowblocks;
-  const int t = threadIdx.x;
-  if (t < B) sh[t] = a.context_lens[t];
-  __syncthreads();
-  const int w = t < B ? sh[t] : 0;
-  int rank = 0, lo = 0x7fffffff, hi = -0x7fffffff;
-  for (int u = 0; u < B; ++u) {
-    const int x = sh[u];
-    rank += (x > w) || (x == w && u < t);
-    lo = min(lo, x);
-    hi = max(hi, x);
-  }
-  if ((long)hi <= (long)lo + lo / 4) {   // uniform: all threads agree (same loads)
-    __syncthreads();                      // the body reuses the LDS
-    return false;
-  }
-  if (t < B) sh[kPrefillSortMaxBatch + rank] = t;   // the sequence of each rank
-  __syncthreads();
-  const long n = (long)B * H * R;
-  const long i = blockIdx.x + (long)B * (blockIdx.y + (long)H * blockIdx.z);
-  const long p = i < kPrefillFirstRound ? i : n - 1 + kPrefillFirstRound - i;   // sorted position
-  const long per = (long)H * R;
-  const int r = (int)(p / per), q = (int)(p - r * per);
-  b = sh[kPrefillSortMaxBatch + r];
-  rb = R - 1 - q / H;
-  g = q % H;
-  __syncthreads();   // the body reuses the LDS
-  return true;
-}
-
 template <int D, int KV, bool QSPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * PrefillLds<D>::stage];
   int b = blockIdx.x, g = blockIdx.y;
   int rb = a.nrowblocks - 1 - (int)blockIdx.z;   // heavier (later) row blocks first
-  if (a.batch <= kPrefillSortMaxBatch) prefill_item(a, reinterpret_cast<int*>(lds), b, g, rb);
+  const long id = blockIdx.x + (long)a.batch * (blockIdx.y + (long)a.hkv * blockIdx.z);
+  if (a.batch <= kPrefillSortMaxBatch && (long)a.batch * a.hkv * a.nrowblocks <= kPrefillSortMaxGrid)
+    prefill_item(a, reinterpret_cast<int*>(lds), id, b, g, rb);
   prefill_body<D, KV, QSPLIT>(a, lds, b, g, rb);
 }
 

@@ -69,6 +69,85 @@ __device__ __forceinline__ int k_swizzle(int rr) {
 
 constexpr float kLazyRescale = 8.0f;
 
+// Which row block a prefill workgroup takes.  Workgroup ids are dealt round
+// robin to the XCDs and, within one, to its CUs in turn, and two workgroups
+// share a CU; a row block's time grows with its sequence's context.  In the
+// grid order (sequence fastest, then KV head, then row block, heavier row
+// blocks first) each sequence's row blocks share one XCD and its L2.  When
+// the whole grid fits two workgroups per CU (at most kPrefillSortMaxGrid;
+// larger grids queue, and the queue balances them) and holds at most
+// kPrefillSortMaxBatch sequences whose contexts differ (among those with
+// rows, the longest more than 25% above the shortest), every workgroup
+// ranks the sequences by context length (ties by index)
+// from the same loads, so all agree on one order of the row blocks that
+// hold rows: the first kPrefillFirstRound ids (one per CU of a 256-CU
+// MI355X) take the heaviest and the next ids the rest lightest first, so
+// that a CU's second workgroup tends to be a light one and every XCD gets a
+// share of the long sequences; ids past the last such row block have no work.
+constexpr int kPrefillSortMaxBatch = 256;
+constexpr long kPrefillFirstRound = 256;
+constexpr long kPrefillSortMaxGrid = 2 * kPrefillFirstRound;
+
+// `id` is the workgroup's position in the grid order.  Returns false (and
+// leaves b, g, rb alone) when the grid order is kept; a workgroup left
+// without work gets rb = nrowblocks, which prefill_body turns away.  Called
+// by all 256 threads; uses 3 KB of `sh`, free again on return.
+__device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int* sh, long id, int& b,
+                                             int& g, int& rb) {
+  const int B = a.batch, H = a.hkv, R = a.nrowblocks;
+  int* weight = sh;                                 // per sequence: context, -1 without rows
+  int* seq_of = sh + kPrefillSortMaxBatch;          // per rank: sequence
+  int* items_of = sh + 2 * kPrefillSortMaxBatch;    // per rank: row blocks holding rows x H
+  const int t = threadIdx.x;
+  int items = 0;
+  if (t < B) {
+    // the rows prefill_body gives the sequence (the same clamping)
+    int C = a.cu_q_lens[t + 1] - a.cu_q_lens[t];
+    C = C < 0 ? 0 : min(C, a.max_q_len);
+    const int rows = (a.skip_single && C == 1) ? 0 : C * a.group;
+    items = (rows + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock * H;
+    weight[t] = items > 0 ? max(a.context_lens[t], 0) : -1;
+  }
+  __syncthreads();
+  const int w = t < B ? weight[t] : 0;
+  int rank = 0, live = 0, lo = 0x7fffffff, hi = -1;
+  for (int u = 0; u < B; ++u) {
+    const int x = weight[u];
+    rank += (x > w) || (x == w && u < t);
+    if (x >= 0) {
+      ++live;
+      lo = min(lo, x);
+      hi = max(hi, x);
+    }
+  }
+  if (live == 0 || (long)hi <= (long)lo + lo / 4) {   // all threads agree (same loads)
+    __syncthreads();
+    return false;
+  }
+  if (t < B) {
+    seq_of[rank] = t;
+    items_of[rank] = items;
+  }
+  __syncthreads();
+  long n_items = 0;
+  for (int r = 0; r < B; ++r) n_items += items_of[r];
+  if (id >= n_items) {
+    rb = R;
+  } else {
+    long p = id;                                   // position in the ranked order
+    if (id >= kPrefillFirstRound) p = n_items - 1 + kPrefillFirstRound - id;
+    long acc = 0;
+    int r = 0;
+    while (p >= acc + items_of[r]) acc += items_of[r++];
+    const int q = (int)(p - acc);
+    b = seq_of[r];
+    rb = items_of[r] / H - 1 - q / H;              // heavier (later) row blocks first
+    g = q % H;
+  }
+  __syncthreads();
+  return true;
+}
+
 // One row block: the 128 rows rb of (sequence b, KV head g).  Called by all
 // 256 threads of the workgroup; `lds` holds two tile stages (1024-aligned).
 template <int D, int KV, bool QSPLIT>
