@@ -252,7 +252,52 @@ def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
         "plan_workspace_bytes": int(nws),
     }
     res["hbm_frac_step"] = res["kv_gbs"] / HBM_PEAK_GBS
+    if name == "C2":
+        res["paged_overhead"] = paged_overhead(g, w, pool, decode, out, q, ws, steps, warmup)
     return w, res, out
+
+
+def paged_overhead(g: Gpu, w, pool, decode_scattered, out_scattered, q, ws, steps, warmup):
+    """The plain decode call over the same K/V gathered into consecutive
+    pages (identity block table: sequence b's logical page i at physical
+    page off_b + i) against the scattered pool; the two outputs must agree
+    bit for bit (same kernels, same plan, only the page addresses differ).
+    Context: TinyLoop's table "KV cache modes" lists paged attention with
+    16-token pages at 5.6% overhead."""
+    torch = g.torch
+    k, v, _, _ = pool
+    npg = (w.context_lens.astype(np.int64) + 15) // 16
+    off = np.concatenate([[0], np.cumsum(npg)[:-1]])
+    src = np.concatenate([w.block_tables[b, :npg[b]] for b in range(w.batch)]).astype(np.int64)
+    src_t = g.t(src)
+    k_id, v_id = k.index_select(0, src_t), v.index_select(0, src_t)
+    bt_id = np.zeros_like(w.block_tables)
+    for b in range(w.batch):
+        bt_id[b, :npg[b]] = off[b] + np.arange(npg[b])
+    bt_id_t, cl = g.t(bt_id), g.t(w.context_lens)
+    out_id = torch.empty_like(out_scattered)
+    ws_id = torch.zeros_like(ws)
+
+    def decode_identity():
+        g.pkv.paged_attn_decode(q, k_id, v_id, bt_id_t, cl, w.max_context_len, w.scale, out=out_id,
+                                workspace=ws_id)
+
+    def one_call(inner, e1=None, e2=None):
+        if e1 is not None:
+            e1.record()
+        inner()
+        if e2 is not None:
+            e2.record()
+
+    log("[bench] C2: paged overhead (identity block table vs scattered pages)")
+    _, sc_ms, _ = g.timed_steps(one_call, decode_scattered, steps, warmup)
+    _, id_ms, _ = g.timed_steps(one_call, decode_identity, steps, warmup)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out_id.view(torch.int32), out_scattered.view(torch.int32)))
+    ss, si = stats(sc_ms), stats(id_ms)
+    return {"scattered_call_ms": ss, "identity_call_ms": si,
+            "overhead": ss["mean"] / si["mean"] - 1.0, "outputs_bit_identical": same,
+            "pages": int(npg.sum())}
 
 
 def bench_prefill(g: Gpu, steps: int, warmup: int):
