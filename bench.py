@@ -101,6 +101,21 @@ def profiled_traffic(profile_name: str, sha: str):
     return float(m_tr.group(1))
 
 
+def profiled_mfma_busy(profile_name: str, sha: str):
+    """MFMA busy fraction from a committed counter summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD x 1024 SIMDs), if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"^source_sha256:\s*(\S+)", text, re.M)
+    m_u = re.search(r"^mfma_busy_frac:\s*([0-9.eE+-]+)", text, re.M)
+    if not m_sha or not m_u or m_sha.group(1) != sha:
+        return None
+    return float(m_u.group(1))
+
+
 class Gpu:
     def __init__(self):
         import torch
@@ -346,7 +361,10 @@ def bench_prefill(g: Gpu, steps: int, warmup: int):
                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": res["tflops_prefill_call"] / BF16_PEAK_TFLOPS,
                        "traffic": profiled_traffic("prefill_C4_counters.txt",
-                                                   source_sha("prefill.hip", "prefill_body.h", "pkv_device.h", "pkv_host.h"))}
+                                                   source_sha("prefill.hip", "prefill_body.h", "pkv_device.h", "pkv_host.h")),
+                       "mfma_busy_frac_counters": profiled_mfma_busy(
+                           "prefill_C4_mfma.txt",
+                           source_sha("prefill.hip", "prefill_body.h", "pkv_device.h", "pkv_host.h"))}
     return w, res, out
 
 
