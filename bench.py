@@ -480,6 +480,16 @@ def bench_rope(g: Gpu, steps: int, warmup: int):
     }
 
 
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, gpu_out, budget_s: float):
     """The oracle as it stands, timed on the host: one step = oracle append
     of the step's new tokens + oracle decode of the whole batch, repeated
@@ -587,7 +597,11 @@ def main():
         })
     line["extra"] = extras
     if head is not None and not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w2, out2, args.cpu_budget)
+        cb = cpu_baseline(w2, out2, args.cpu_budget)
+        cb["cpu_model"] = cpu_model()
+        # a reported baseline, not a target: the oracle is plain fp64 numpy
+        cb["gpu_step_speedup"] = cb["seconds_per_step"] / (head["ms_per_step"] * 1e-3)
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 
