@@ -540,8 +540,9 @@ def main():
                     help="comma list of workloads to run (C1..C5, M1, M2, R1, W1, F1); default all")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(decode and prefill shard by sequence or KV head with no exchange); "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2", "R1",
                                                         "W1", "F1"}
