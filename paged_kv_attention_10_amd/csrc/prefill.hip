@@ -38,8 +38,8 @@
 //
 // Precision: q and K/V in the cache's 16-bit type (an fp32 or other-typed
 // q is split into head + remainder and multiplied twice), P rounded to the
-// 16-bit type for PV (the normaliser sums the fp32 values), fp32
-// accumulation.
+// 16-bit type for PV (the normaliser sums those same rounded values, two
+// per packed dot product), fp32 accumulation.
 #include "prefill_body.h"
 
 namespace pkv {

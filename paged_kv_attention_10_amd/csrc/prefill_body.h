@@ -13,6 +13,7 @@
 namespace pkv {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -386,9 +387,20 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][r], a.scale_log2, -m_use));
-        lsum += p;
         if constexpr (kBF16) p16[r >> 3][r & 7] = (__bf16)p;
         else p16[r >> 3][r & 7] = (_Float16)p;
+      }
+      // the row sum takes the rounded probabilities the PV multiplies, two
+      // per packed dot product with (1, 1)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        if constexpr (kBF16) {
+          const bf16x2 pair = {p16[r >> 3][r & 7], p16[r >> 3][(r & 7) + 1]};
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.f, (__bf16)1.f}, lsum, false);
+        } else {
+          const f16x2 pair = {p16[r >> 3][r & 7], p16[r >> 3][(r & 7) + 1]};
+          lsum = __builtin_amdgcn_fdot2(pair, f16x2{(_Float16)1.f, (_Float16)1.f}, lsum, false);
+        }
       }
       // ---- O^T += V^T * P^T
 #pragma unroll
