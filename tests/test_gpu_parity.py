@@ -220,13 +220,16 @@ def test_prefill_config_full_size(pkv):
     assert err <= 1e-2
 
 
-@pytest.mark.parametrize("case", ["spread_many_blocks", "spread_few_blocks", "uniform", "batch_over_256"])
+@pytest.mark.parametrize("case", ["spread_many_blocks", "spread_few_blocks", "uniform", "batch_over_256",
+                                  "batch_256_grid_512"])
 def test_prefill_row_block_order(pkv, case):
     """Every row block is computed exactly once whichever order the workgroups
     take them in: contexts that differ (ranked order, with more and with fewer
     row blocks than the first round of 256 workgroups), contexts within 25% of
     each other (grid order) and more than 256 sequences (grid order).  The
-    output starts as NaN, so a row no workgroup wrote fails."""
+    output starts as NaN, so a row no workgroup wrote fails.  The last case is
+    the largest grid that takes the ranked order: 256 sequences, 512
+    workgroups."""
     rng = np.random.Generator(np.random.PCG64(77))
     if case == "spread_many_blocks":       # 12 sequences x 2 KV heads x 12 row blocks = 288 > 256
         ql = [256] * 12
@@ -240,9 +243,13 @@ def test_prefill_row_block_order(pkv, case):
         ql = [128] * 10
         pre = [500 + 10 * i for i in range(10)]
         hq, hkv = 6, 2
-    else:
+    elif case == "batch_over_256":
         ql = rng.integers(1, 6, size=300).tolist()
         pre = rng.integers(0, 120, size=300).tolist()
+        hq, hkv = 4, 2
+    else:                                  # the largest ranked grid: 256 x 2 KV heads x 1 row block
+        ql = rng.integers(1, 9, size=256).tolist()
+        pre = rng.integers(0, 300, size=256).tolist()
         hq, hkv = 4, 2
     ctx = [p + c for p, c in zip(pre, ql)]
     w = small_prefill(ctx, ql, hq, hkv, 64, "bf16", seed=len(ctx))
