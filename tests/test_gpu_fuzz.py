@@ -158,6 +158,25 @@ def test_prefill_output_dtypes_and_bad_page(pkv):
     assert oracle.max_abs_err(out[:100], ref[:100]) <= 1e-2
 
 
+def test_prefill_bad_context_length_gives_nan(pkv):
+    """A context length past max_context_len (device data the host cannot
+    check) turns that sequence's rows into NaN and leaves the others exact,
+    also when the workgroups take the row blocks in ranked order (the
+    contexts differ, so the bad value takes part in the ranking)."""
+    w = small_prefill([200, 60, 130], [64, 60, 30], 6, 2, 64, "bf16", seed=95)
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w, "bf16")
+    ref = oracle.ref_prefill_chunk(q_exact_values(q), cache, w.block_tables, w.context_lens,
+                                   w.cu_q_lens, w.scale)
+    w.context_lens[1] = 10 ** 6
+    out = run_prefill(pkv, w, gc, q, max_context_len=200).cpu().numpy().astype(np.float64)
+    lo, hi = int(w.cu_q_lens[1]), int(w.cu_q_lens[2])
+    assert np.all(np.isnan(out[lo:hi]))
+    keep = np.r_[0:lo, hi:out.shape[0]]
+    assert oracle.max_abs_err(out[keep], ref[keep]) <= 1e-2
+
+
 def test_decode_bad_context_length_gives_nan(pkv):
     w = small_decode([40, 50], 4, 2, 64, "bf16", seed=94)
     cache = oracle_cache(w)
