@@ -79,9 +79,9 @@ constexpr float kLazyRescale = 8.0f;
 // larger grids queue, and the queue balances them) and holds at most
 // kPrefillSortMaxBatch sequences whose contexts differ (among those with
 // rows, the longest more than 25% above the shortest), every workgroup
-// ranks the sequences by context length (ties by index)
-// from the same loads, so all agree on one order of the row blocks that
-// hold rows: the first kPrefillFirstRound ids (one per CU of a 256-CU
+// ranks the sequences by context length (ties by index) from the same
+// loads, so all agree on one order of the row blocks that hold rows: the
+// first kPrefillFirstRound ids (one per CU of a 256-CU
 // MI355X) take the heaviest and the next ids the rest lightest first, so
 // that a CU's second workgroup tends to be a light one and every XCD gets a
 // share of the long sequences; ids past the last such row block have no work.
