@@ -376,8 +376,17 @@ def ref_prefill_chunk(q, cache: PagedCache, block_tables, context_lens, cu_q_len
 
 # ---------------------------------------------------------------- comparison
 def max_abs_err(gpu_out, ref) -> float:
-    """max |gpu - ref| over all elements; NaN/inf anywhere -> inf."""
+    """The parity measure: max |gpu - ref| over every element, each side
+    widened to fp64 before the difference.  The two arrays must have the
+    same shape (no broadcasting: a missing axis is an error, not a smaller
+    comparison).  A NaN or an infinity on either side gives +inf, so such an
+    output fails every tolerance.  Empty arrays give 0."""
     g = np.asarray(gpu_out, dtype=np.float64)
-    if not np.all(np.isfinite(g)):
+    r = np.asarray(ref, dtype=np.float64)
+    if g.shape != r.shape:
+        raise ValueError(f"compared arrays differ in shape: {g.shape} vs {r.shape}")
+    if g.size == 0:
+        return 0.0
+    if not (np.all(np.isfinite(g)) and np.all(np.isfinite(r))):
         return float("inf")
-    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+    return float(np.max(np.abs(g - r)))

@@ -617,4 +617,43 @@ def pin_fp8_bounds(O):
     assert np.array_equal(s2, sc) and np.array_equal(c2 ^ 0x80, codes)
 
 
+def pin_comparator(O):
+    """max_abs_err, the measure every parity test asserts through, against
+    values fixed by hand: a difference of either sign counts by its
+    magnitude, one large element is not averaged away among equal ones, both
+    sides are widened to fp64 before the difference (fp32 0.1 differs from
+    fp64 0.1 by 2^-27 * 0.2 exactly), a NaN or an infinity on either side
+    gives +inf, and arrays of different shapes are refused rather than
+    broadcast."""
+    r = np.linspace(-1.0, 1.0, 1000).reshape(10, 100)
+    assert O.max_abs_err(r.copy(), r) == 0.0
+    g = r.copy()
+    g[3, 7] -= 0.5                       # gpu below the reference
+    assert O.max_abs_err(g, r) == 0.5
+    g = r.copy()
+    g[9, 99] += 0.25                     # one element among 1000
+    assert O.max_abs_err(g, r) == 0.25
+    g = r.copy()
+    g[0, 0] += 0.125
+    g[5, 5] -= 0.375
+    assert O.max_abs_err(g, r) == 0.375  # the largest magnitude, not the largest signed value
+    x32 = np.float32(0.1)
+    exact = abs(float(x32) - 0.1)
+    assert exact > 0 and O.max_abs_err(np.array([x32]), np.array([0.1])) == exact
+    for bad in (np.nan, np.inf, -np.inf):
+        g = r.copy()
+        g[2, 2] = bad
+        assert O.max_abs_err(g, r) == float("inf")
+        rr = r.copy()
+        rr[4, 4] = bad
+        assert O.max_abs_err(r.copy(), rr) == float("inf")
+    assert O.max_abs_err(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+    for shape in ((100,), (1, 10, 100), (10, 1), (100, 10)):
+        try:
+            O.max_abs_err(np.zeros(shape), r)
+        except ValueError:
+            continue
+        raise AssertionError(f"shape {shape} against {r.shape} was compared")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

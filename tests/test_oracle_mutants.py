@@ -71,6 +71,16 @@ MUTANTS = [
      "return storage_from_f32(np.asarray(q, dtype=np.float32), dtype)"),
     ("rope_frequency_half_precision", ".astype(np.float32).astype(np.float64)\n    ang",
      ".astype(np.float16).astype(np.float64)\n    ang"),
+    ("comparator_signed", "return float(np.max(np.abs(g - r)))", "return float(np.max(g - r))"),
+    ("comparator_mean", "return float(np.max(np.abs(g - r)))", "return float(np.mean(np.abs(g - r)))"),
+    ("comparator_fp32", "return float(np.max(np.abs(g - r)))",
+     "return float(np.max(np.abs(g.astype(np.float32) - r.astype(np.float32))))"),
+    ("comparator_gpu_only_finite", "np.all(np.isfinite(g)) and np.all(np.isfinite(r))",
+     "np.all(np.isfinite(g))"),
+    ("comparator_ignores_nan", "np.all(np.isfinite(g)) and np.all(np.isfinite(r))",
+     "not np.any(np.isinf(g)) and not np.any(np.isinf(r))"),
+    ("comparator_broadcasts", "    if g.shape != r.shape:\n        raise",
+     "    if g.ndim != r.ndim and False:\n        raise"),
     ("rope_f16_intermediate", "ref_append(cache, k_rot.astype(np.float32), v_new, slot_mapping)",
      "ref_append(cache, k_rot.astype(np.float16).astype(np.float32), v_new, slot_mapping)"),
 ]
