@@ -372,20 +372,9 @@ def mixed_workload(name):
     """M1: C2's 64 decode sequences and C4's eight 512-token chunks in one
     batch.  M2 (decode-heavy): C2's 64 decode sequences and four 64-token
     chunks over 1024-token prefixes.  Same heads, head_dim 128, bf16 q and
-    KV, seeded draw."""
-    from workloads import custom_workload, make_workload
-    w2 = make_workload("C2")
-    if name == "M1":
-        w4 = make_workload("C4")
-        chunks = [(int(c), int(q)) for c, q in zip(w4.context_lens, w4.q_lens)]
-    else:
-        chunks = [(1024 + 64, 64)] * 4
-    ctx = [int(x) for x in w2.context_lens] + [c for c, _ in chunks]
-    q_lens = [1] * w2.batch + [q for _, q in chunks]
-    return custom_workload(kind="prefill", context_lens=ctx, q_lens=q_lens, num_q_heads=12,
-                           num_kv_heads=2, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
-                           num_pages=20000, table_width=256, seed=6 if name == "M1" else 7,
-                           name=name)
+    KV, seeded draw (workloads.make_workload)."""
+    from workloads import make_workload
+    return make_workload(name)
 
 
 def bench_mixed(g: Gpu, name: str, steps: int, warmup: int):

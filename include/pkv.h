@@ -105,8 +105,10 @@ const char* pkv_status_string(int status);
  * clamp(rint(x/scale), -127, 127) with ties to even, scale 0 and codes 0 for
  * an all-zero vector; FP8 likewise with scale = absmax/448 and code = the
  * E4M3 value nearest to clamp(x/scale, -448, 448) (ties to even; the sign
- * bit is that of the fp32 ratio, so -0 stores 0x80).  The int8 and FP8
- * results for a vector holding inf or NaN are unspecified.  num_tokens == 0
+ * bit is that of the fp32 ratio, so -0 stores 0x80).  An int8 or FP8
+ * vector holding a NaN stores scale NaN and codes 0 (attention over that
+ * token then gives NaN); one holding an infinity (and no NaN) stores scale
+ * +inf with unspecified codes.  num_tokens == 0
  * is a no-op returning PKV_OK.
  */
 int paged_kv_append(const void* k_new, const void* v_new, int new_dtype,
@@ -182,7 +184,8 @@ int paged_kv_append_rope(const void* k_new, const void* v_new, int new_dtype,
  *   max_context_len  host-side upper bound of context_lens, at most
  *                  max_blocks_per_seq*16; sizes the split of long contexts.
  *   num_pages      pool size in pages (page ids must be below it).
- *   scale          multiplies q.k before the softmax.
+ *   scale          multiplies q.k before the softmax; any finite value
+ *                  (negative and zero included), else PKV_ERR_INVALID_ARG.
  *   window         0 for the whole context, or a sliding window of `window`
  *                  tokens (TinyLoop "Current Status", table "KV cache modes",
  *                  row "Sliding-window cache"): the query at position

@@ -20,7 +20,10 @@
 // workgroup builds the RoPE angle table of its tokens once in LDS.  int8
 // takes the absmax of the (token, head) row with a shuffle over the row's
 // lanes, then scale = absmax/127 (IEEE fp32 division) and
-// code = clamp(rint(x/scale), -127, 127) with ties to even.
+// code = clamp(rint(x/scale), -127, 127) with ties to even.  The absmax is
+// taken on the bit patterns so that a NaN element gives a NaN scale (and
+// codes 0): attention over such a token comes out NaN instead of reading
+// plausible codes.
 //
 // RoPE: coordinate pair i turns by pos * f_i radians, f_i = theta^(-2i/D)
 // held as an fp32 number (the power evaluated in double and rounded once,
@@ -222,11 +225,12 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
     const long head = page * a.hkv + h;
     uint32_t bits[16];
     if (kv_scaled(a.cache_dtype)) {
-      float am = 0.f;
+      uint32_t amk = 0u;   // absmax as a sort key: a NaN element makes the scale NaN
 #pragma unroll
-      for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(x[j]));
+      for (int j = 0; j < 16; ++j) amk = max(amk, abs_key(x[j]));
 #pragma unroll
-      for (int m = 1; m < NSEG; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+      for (int m = 1; m < NSEG; m <<= 1) amk = max(amk, (uint32_t)__shfl_xor((int)amk, m));
+      const float am = __uint_as_float(amk);
       if (a.cache_dtype == PKV_I8) {
         const float sc = am / 127.0f;
 #pragma unroll
@@ -328,11 +332,12 @@ __device__ __forceinline__ void row_append(const AppendArgs& a, const void* src,
     return is_v ? (head * D + d) * kPage + off : (head * kPage + off) * D + d;
   };
   if (kv_scaled(a.cache_dtype)) {
-    float am = 0.f;
+    uint32_t amk = 0u;   // absmax as a sort key: a NaN element makes the scale NaN
 #pragma unroll
-    for (int e = 0; e < PER; ++e) am = fmaxf(am, fabsf(x[e]));
+    for (int e = 0; e < PER; ++e) amk = max(amk, abs_key(x[e]));
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) am = fmaxf(am, __shfl_xor(am, m));
+    for (int m = 32; m >= 1; m >>= 1) amk = max(amk, (uint32_t)__shfl_xor((int)amk, m));
+    const float am = __uint_as_float(amk);
     const bool i8 = a.cache_dtype == PKV_I8;
     const float sc = am / (i8 ? 127.0f : 448.0f);
 #pragma unroll

@@ -148,7 +148,7 @@ static int decode_call(const void* q, int q_dtype, const void* k_cache, const vo
       (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE || batch > 65535 ||
       window < 0)
     return PKV_ERR_INVALID_ARG;
-  if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
+  if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype) || !scale_ok(scale))
     return PKV_ERR_INVALID_ARG;
   if (kv_scaled(kv_dtype) != (k_scales != nullptr) || kv_scaled(kv_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;

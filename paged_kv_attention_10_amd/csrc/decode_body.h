@@ -272,8 +272,10 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
                                                       int gy, int b) {
   constexpr bool kF32 = (KV == PKV_F32);
   constexpr bool kI8 = kv_code8(KV);   // int8 or FP8 codes, exact in fp16
-  // an FP8 code converts to 2^-8 times its value; the 2^8 goes on the scales
+  // an FP8 code converts to 2^-8 times its value; the 2^8 goes on the K
+  // scales and, for V, into the final power-of-two rescale
   constexpr float kCodeScale = (KV == PKV_FP8) ? 256.0f : 1.0f;
+  constexpr int kVShift = (KV == PKV_FP8) ? 8 : 0;
   constexpr bool kBF16 = (KV == PKV_BF16);
   using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
   constexpr int NSTEP = kF32 ? D / 4 : D / 32;    // QK MFMA k-steps
@@ -410,6 +412,9 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   for (int i = 0; i < NBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_part = 0.f;
+  // 8-bit caches: acc holds the output times 2^-(v_exp - 4 + kVShift), where
+  // v_exp is the binade of the largest V scale seen (see compute)
+  int v_exp = -1000;
 
   auto issue = [&](DecodeTile<D, KV>& dst, int li) {
     const int pa = __builtin_amdgcn_readlane(pid, 2 * li);
@@ -508,12 +513,37 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
       }
     } else {
       float pv[8];
+      if constexpr (kI8) {
+        // The V scale folds into the probability, which the PV MFMA takes
+        // as fp16 (head + remainder).  To keep p * scale inside fp16's range
+        // for any scale, the scales are multiplied by 2^(4 - v_exp), v_exp
+        // being the binade of the largest in-context scale the wave has met
+        // (wave-uniform; raised, and the accumulator scaled down by the same
+        // power of two, only when a tile's largest scale lies more than two
+        // binades above it): p <= 2^8 under the lazy max, so p * scale stays
+        // below 2^14.  Scales of masked tokens may hold anything and are
+        // left out.
+        float vsc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = p[e];
-        if constexpr (kI8)
-          x = (tok0 + e < ctx && tok0 + e >= lo) ? x * (cur.vs[e >> 2][e & 3] * kCodeScale) : 0.f;
-        pv[e] = x;
+        for (int e = 0; e < 8; ++e)
+          vsc[e] = (tok0 + e < ctx && tok0 + e >= lo) ? cur.vs[e >> 2][e & 3] : 0.f;
+        float vmax = vsc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) vmax = fmaxf(vmax, vsc[e]);
+        vmax = wave_max_xor_16_32(vmax);
+        const int et = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(vmax));
+        if (et > v_exp + 2) {
+#pragma unroll
+          for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_ldexpf(acc[i][r], v_exp - et);
+          v_exp = et;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = p[e] * __builtin_ldexpf(vsc[e], 4 - v_exp);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = p[e];
       }
       // V of tokens at or past the context end or before the window may
       // hold anything: zero them
@@ -598,6 +628,12 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
     }
   }
   const float l_run = wave_sum_xor_16_32(l_part);
+  if constexpr (kI8) {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_ldexpf(acc[i][r], v_exp - 4 + kVShift);
+  }
 
   // ---- merge the four waves in LDS
   typedef float OrowT[16][D + 1];
@@ -626,6 +662,11 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 #pragma unroll
     for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][hc]);
     float num = 0.f, den = 0.f;
+    // a NaN score (e.g. a token whose K scale is NaN) makes a wave's sum NaN
+    // while the max skips it: such a row is NaN, not zero
+    bool nan_l = false;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) nan_l |= s_l[w][hc] != s_l[w][hc];
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) {
@@ -634,15 +675,16 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
         den += s_l[w][hc] * f;
       }
     }
+    const bool poison = any_bad || nan_l;
     float val = den > 0.f ? num / den : 0.f;
-    if (any_bad) val = NAN;
+    if (poison) val = NAN;
     const long row = (long)b * a.hq + h0 + hc;
     if (direct) {
       store_from_f32(a.out, ((long)qb * a.hq + h0 + hc) * D + d, a.out_dtype, val);
     } else {
       const long prow = row * a.nsplits + split;
       a.part_o[prow * D + d] = val;
-      if (d == 0) a.part_lse[prow] = any_bad ? NAN : (den > 0.f ? M + log2f(den) : -INFINITY);
+      if (d == 0) a.part_lse[prow] = poison ? NAN : (den > 0.f ? M + log2f(den) : -INFINITY);
     }
   }
 }

@@ -114,7 +114,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
       max_context_len < 0 || max_q_len > max_context_len || batch > 65535 || window < 0 ||
       (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE)
     return PKV_ERR_INVALID_ARG;
-  if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
+  if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype) || !scale_ok(scale))
     return PKV_ERR_INVALID_ARG;
   if (kv_scaled(kv_dtype) != (k_scales != nullptr) || kv_scaled(kv_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
@@ -182,7 +182,11 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   pa.group = num_q_heads / num_kv_heads;
   pa.num_pages = num_pages;
   pa.nrowblocks = ceil_div((long)max_q_len * pa.group, kPrefillRowsPerBlock);
-  pa.scale_log2 = scale * kLog2e;
+  const ScaleForm sf = scale_form(scale, kLog2e);
+  pa.scale_log2 = sf.c;
+  pa.q_xor = sf.q_xor;
+  pa.q_and = sf.q_and;
+  pa.q_mul = sf.q_mul;
   pa.skip_single = 1;
   pa.window = window;
   if (pa.nrowblocks > 65535) return PKV_ERR_INVALID_ARG;

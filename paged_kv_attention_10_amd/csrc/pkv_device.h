@@ -194,6 +194,12 @@ __device__ __forceinline__ Split8<f16x8> split_f16(const float (&x)[8]) {
   return r;
 }
 
+// Sort key of |x|: for non-negative floats the unsigned order of the bit
+// patterns is the numeric order, and every NaN pattern lies above +inf, so
+// the unsigned max of these keys over a vector is its absmax, or a NaN when
+// any element is NaN (an fmax would skip the NaN).
+__device__ __forceinline__ uint32_t abs_key(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
 // int8 codes (4 per dword) -> fp16, exact.  Flipping the sign bit turns a
 // code x into the byte x + 128; v_perm places each such byte under the fp16
 // exponent of 1024 (bits 0x64xx), which reads as 1024 + x + 128, and one

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "../../include/pkv.h"
 
 namespace pkv {
@@ -14,6 +16,23 @@ inline bool io_dtype_ok(int dt) { return dt == PKV_F32 || dt == PKV_BF16 || dt =
 __host__ __device__ inline bool kv_scaled(int dt) { return dt == PKV_I8 || dt == PKV_FP8; }
 inline bool kv_dtype_ok(int dt) { return io_dtype_ok(dt) || kv_scaled(dt); }
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+inline bool scale_ok(float scale) { return std::isfinite(scale); }
+
+// The prefill's form of a softmax scale: a positive exponent factor and the
+// query's sign (see PrefillArgs).
+struct ScaleForm {
+  float c;
+  uint32_t q_xor, q_and;
+  float q_mul;
+};
+inline ScaleForm scale_form(float scale, float log2e) {
+  ScaleForm f;
+  f.c = (scale != 0.f ? (scale < 0.f ? -scale : scale) : 1.f) * log2e;
+  f.q_xor = scale < 0.f ? 0x80008000u : 0u;
+  f.q_and = scale != 0.f ? 0xffffffffu : 0u;
+  f.q_mul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
+  return f;
+}
 
 // Clears any stale error, so the check after a launch sees only ours.
 inline void clear_launch_error() { (void)hipGetLastError(); }

@@ -101,7 +101,7 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
       max_context_len < 0 || max_q_len > max_context_len || window < 0 ||
       (long)max_context_len > (long)max_blocks_per_seq * PKV_PAGE_SIZE)
     return PKV_ERR_INVALID_ARG;
-  if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype))
+  if (!io_dtype_ok(q_dtype) || !io_dtype_ok(out_dtype) || !kv_dtype_ok(kv_dtype) || !scale_ok(scale))
     return PKV_ERR_INVALID_ARG;
   if (kv_scaled(kv_dtype) != (k_scales != nullptr) || kv_scaled(kv_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
@@ -131,7 +131,11 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
   a.group = num_q_heads / num_kv_heads;
   a.num_pages = num_pages;
   a.nrowblocks = ceil_div((long)max_q_len * a.group, kPrefillRowsPerBlock);
-  a.scale_log2 = scale * kLog2e;
+  const ScaleForm sf = scale_form(scale, kLog2e);
+  a.scale_log2 = sf.c;
+  a.q_xor = sf.q_xor;
+  a.q_and = sf.q_and;
+  a.q_mul = sf.q_mul;
   a.skip_single = 0;
   a.window = window;
   if (a.nrowblocks > 65535 || batch > 0x7fffffff) return PKV_ERR_INVALID_ARG;

@@ -45,7 +45,13 @@ struct PrefillArgs {
   int q_dtype, out_dtype;
   int max_blocks, max_context_len, max_q_len;
   int batch, hq, hkv, group, num_pages, nrowblocks;
+  // scale * log2(e) enters as c = |scale| * log2(e) > 0 (log2(e) for a zero
+  // scale) with the query multiplied by the sign of the scale (0 for a zero
+  // scale) as it is loaded: exact, and the raw-score max and the -inf masks
+  // below then need a positive c
   float scale_log2;
+  uint32_t q_xor, q_and;   // applied to packed 16-bit query words
+  float q_mul;             // applied to an fp32 query value
   int skip_single;   // mixed batch: chunks of one token are left to the decode path
   int window;        // sliding window in tokens, 0 = the whole causal prefix
 };
@@ -209,6 +215,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
       const int d0 = 16 * s + 8 * hh;
       u32x4 w = live ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + qrow + d0)
                      : u32x4{0u, 0u, 0u, 0u};
+      w = (w ^ a.q_xor) & a.q_and;
       qhi[s] = __builtin_bit_cast(H8, w);
     }
   } else {
@@ -222,7 +229,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
       for (int s = 0; s < NSTEP; ++s) {
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? io_value<QT>(bits[s][e]) : 0.f;
+        for (int e = 0; e < 8; ++e) x[e] = live ? io_value<QT>(bits[s][e]) * a.q_mul : 0.f;
         if constexpr (kBF16) {
           auto sp = split_bf16(x);
           qhi[s] = sp.hi;
@@ -429,7 +436,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
 
   const float l_run = sum_xor32(l_part);
   if (!live) return;
-  const float inv = bad ? NAN : (l_run > 0.f ? 1.f / l_run : 0.f);
+  // a NaN score makes the row sum NaN while the max skips it: NaN, not zero
+  const float inv = (bad || l_run != l_run) ? NAN : (l_run > 0.f ? 1.f / l_run : 0.f);
   const long orow = ((long)(q0 + pos) * a.hq + h) * D;
   // lane (col + 32*hh), register r of block db holds d = 32*db + 8*(r/4) + 4*hh + r%4:
   // four consecutive d per group of four registers

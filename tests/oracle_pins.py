@@ -656,4 +656,24 @@ def pin_comparator(O):
         raise AssertionError(f"shape {shape} against {r.shape} was compared")
 
 
+def pin_quantizers_non_finite(O):
+    """A NaN anywhere in a vector makes its int8/FP8 scale NaN and its codes
+    0; an infinity makes the scale +inf; other rows of the same call are
+    untouched (the library's stated handling of non-finite inputs)."""
+    import warnings
+    rng = np.random.default_rng(93)
+    x = rng.standard_normal((4, 64)).astype(np.float32)
+    x[1, 9] = np.nan
+    x[2, 0] = -np.inf
+    clean = np.delete(x, [1, 2], axis=0)
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        for quant in (O.quantize_int8, O.quantize_fp8):
+            codes, sc = quant(x)
+            assert np.isnan(sc[1]) and np.all(codes[1].view(np.uint8) == 0)
+            assert sc[2] == np.inf
+            c0, s0 = quant(clean)
+            assert np.array_equal(s0, sc[[0, 3]]) and np.array_equal(c0, codes[[0, 3]])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -106,7 +106,8 @@ INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL = 1, 2, 3, 4
     ({"ks": FAKE, "vs": FAKE}, INVALID),                    # scales with a non-int8 KV
     ({"ps": 8}, UNSUPPORTED), ({"d": 96}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED),
     ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest context built
-    ({"win": -1}, INVALID),
+    ({"win": -1}, INVALID), ({"sc": float("nan")}, INVALID), ({"sc": float("inf")}, INVALID),
+    ({"sc": float("-inf")}, INVALID),
     ({"q": FAKE + 4}, MISALIGNED), ({"v": FAKE + 8}, MISALIGNED), ({"out": FAKE + 2}, MISALIGNED),
     ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "ws": None, "wsb": 0, "mb": 256}, WS_SMALL),
     ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "wsb": 1024, "mb": 256}, WS_SMALL),
@@ -124,7 +125,8 @@ def test_decode_rejects(lib, over, code):
     ({"kvd": 0}, UNSUPPORTED), ({"kvd": 3, "ks": FAKE, "vs": FAKE}, UNSUPPORTED),
     ({"kvd": 4, "ks": FAKE, "vs": FAKE}, UNSUPPORTED),
     ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED), ({"cu": FAKE + 4}, MISALIGNED),
-    ({"od": 3}, INVALID), ({"win": -5}, INVALID),
+    ({"od": 3}, INVALID), ({"win": -5}, INVALID), ({"sc": float("nan")}, INVALID),
+    ({"sc": float("-inf")}, INVALID),
 ])
 def test_prefill_rejects(lib, over, code):
     assert _prefill(lib, **over) == code
@@ -138,6 +140,7 @@ def test_prefill_rejects(lib, over, code):
     ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED),
     ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest split context
     ({"cu": FAKE + 4}, MISALIGNED), ({"od": 3}, INVALID), ({"win": -1}, INVALID),
+    ({"sc": float("nan")}, INVALID), ({"sc": float("inf")}, INVALID),
     ({"mcl": 4096, "mb": 256, "B": 64, "hq": 12, "hkv": 2, "d": 128, "mql": 1, "ws": None, "wsb": 0},
      WS_SMALL),
 ])
@@ -215,6 +218,7 @@ def _decode_append(lib, **over):
     ({"kn": None}, INVALID), ({"vn": None}, INVALID), ({"nd": 3}, INVALID), ({"q": None}, INVALID),
     ({"kvd": 3}, UNSUPPORTED), ({"kvd": 4}, UNSUPPORTED), ({"kvd": 5}, INVALID),
     ({"hq": 5}, INVALID), ({"win": -1}, INVALID), ({"d": 96}, UNSUPPORTED),
+    ({"sc": float("nan")}, INVALID),
     ({"kn": FAKE + 4}, MISALIGNED), ({"vn": FAKE + 2}, MISALIGNED),
     ({"mcl": 4096, "B": 64, "hq": 12, "hkv": 2, "d": 128, "wsb": 1024, "mb": 256}, WS_SMALL),
 ])

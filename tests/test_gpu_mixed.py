@@ -10,6 +10,7 @@ import torch
 import oracle
 from gpu_helpers import (np_to_gpu, oracle_cache, poisoned_gpu_cache, q_exact_values, q_tensor,
                          say, small_prefill, to_f64, used_slot_mask)
+from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -112,11 +113,47 @@ def test_mixed_bad_inputs_give_nan_rows(pkv):
     gc = poisoned_gpu_cache(cache, used_slot_mask(w))
     q = q_tensor(w, "bf16")
     good = ref(w, cache, q)
+    page = int(w.block_tables[1, 1])
     w.block_tables[1, 1] = w.num_pages + 3          # decode row 100 reads page 1 (tokens 16..31)
     out = run_mixed(pkv, w, gc, q).cpu().numpy().astype(np.float64)
     assert np.all(np.isnan(out[100])) and np.all(np.isfinite(out[[0, 99, 101]]))
+    assert oracle.max_abs_err(out[:100], good[:100]) <= 1e-2     # the chunk's 100 rows
     assert oracle.max_abs_err(out[101:], good[101:]) <= 1e-2
-    w.block_tables[1, 1] = int(w.block_tables[0, 0])
+    w.block_tables[1, 1] = page
     w.context_lens[2] = 0                            # a one-token chunk longer than its context
-    out = run_mixed(pkv, w, gc, q).cpu().numpy()
+    out = run_mixed(pkv, w, gc, q).cpu().numpy().astype(np.float64)
     assert np.all(np.isnan(out[101]))
+    assert oracle.max_abs_err(out[:101], good[:101]) <= 1e-2
+
+
+@pytest.mark.parametrize("name", ["M1", "M2"])
+def test_mixed_bench_batches_full_size(pkv, name):
+    """The two mixed batches the benchmark times, every row against the
+    oracle: M1 (C2's 64 decode rows and C4's 512-token chunks: long chunks,
+    so the one-token rows take the fewest splits) and M2 (the same decode
+    rows and four 64-token chunks: short chunks, so the one-token rows are
+    split as in a decode call)."""
+    w = make_workload(name)
+    say(f"mixed {name} full size: {w.batch} sequences, {w.num_query_tokens} query rows")
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w, "bf16")
+    out = run_mixed(pkv, w, gc, q)
+    err = oracle.max_abs_err(to_f64(out), ref(w, cache, q))
+    say(f"  max abs err {err:.3e}")
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_mixed_short_chunks_every_row(pkv, d):
+    """Chunks of 2 to 127 tokens beside one-token rows (the plan that splits
+    the one-token rows as a decode call), every row against the oracle."""
+    ctx = [2, 1500, 40, 5, 700, 128, 3000, 17, 260]
+    chunk = [2, 1, 33, 5, 1, 127, 1, 16, 100]
+    w = small_prefill(ctx, chunk, 8, 2, d, "bf16", seed=306)
+    say(f"mixed short chunks d={d}")
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = q_tensor(w, "bf16")
+    out = run_mixed(pkv, w, gc, q)
+    assert oracle.max_abs_err(to_f64(out), ref(w, cache, q)) <= 1e-2

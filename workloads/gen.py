@@ -234,8 +234,31 @@ def _w1(seed):
               "window": window, "first_pos": first.astype(np.int64)})
 
 
+def _mixed(name, seed):
+    """A mixed batch in one varlen call: the C2 decode batch (64 one-token
+    chunks at its context lengths) followed by prefill chunks: M1 takes the
+    C4 chunks (8 x 512 tokens over its prefixes), M2 four 64-token chunks
+    over 1024-token prefixes (a decode-heavy batch whose chunks are short).
+    Qwen2.5-1.5B heads, bf16 q and KV, 20k-page pool, values drawn afresh
+    from `seed`."""
+    w2 = _c2(2)
+    if name == "M1":
+        w4 = _c4(4)
+        chunks = [(int(c), int(q)) for c, q in zip(w4.context_lens, w4.q_lens)]
+    else:
+        chunks = [(1024 + 64, 64)] * 4
+    ctx = [int(x) for x in w2.context_lens] + [c for c, _ in chunks]
+    q_lens = [1] * w2.batch + [q for _, q in chunks]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _build(name, "prefill", rng, ctx, q_lens, 12, 2, 128, "bf16", "bf16", "f32",
+                  20000, 256, seed,
+                  meta={"desc": f"mixed batch {name}: the C2 decode rows + "
+                                + ("the C4 chunks" if name == "M1" else "4 x 64-token chunks over 1024-token prefixes")})
+
+
 CONFIGS = {"C1": (_c1, 1), "C2": (_c2, 2), "C3": (_c3, 3), "C4": (_c4, 4), "C5": (_c5, 5),
-           "W1": (_w1, 8), "F1": (_f1, 2)}
+           "W1": (_w1, 8), "F1": (_f1, 2), "M1": (lambda s: _mixed("M1", s), 6),
+           "M2": (lambda s: _mixed("M2", s), 7)}
 
 
 def make_workload(name: str, seed: Optional[int] = None) -> Workload:
