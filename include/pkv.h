@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 #define PKV_PAGE_SIZE 16
 
 /* Element types.  PKV_BF16 is bfloat16 bits; PKV_I8 (int8 codes) and PKV_FP8
@@ -70,7 +70,9 @@ enum {
   PKV_ERR_UNSUPPORTED = 2,          /* page size, head_dim or dtype combination not built */
   PKV_ERR_MISALIGNED = 3,           /* a tensor pointer is not 16-byte aligned */
   PKV_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace_bytes below the size the query returns */
-  PKV_ERR_HIP = 5                   /* a kernel launch failed */
+  PKV_ERR_HIP = 5,                  /* a kernel launch failed */
+  PKV_ERR_SCRATCH_TOO_SMALL = 6     /* paged_attn_decode_noalloc: the call needs more split
+                                       scratch than PKV_NOALLOC_SCRATCH_BYTES */
 };
 
 typedef struct ihipStream_t* pkv_stream_t; /* the same type as hipStream_t */
@@ -250,6 +252,34 @@ int paged_attn_decode_append(const void* q, int q_dtype,
                              int page_size, int num_pages, float scale, int window,
                              void* out, int out_dtype,
                              void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
+/*
+ * paged_attn_decode_noalloc - paged_attn_decode without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, layouts and results are those of paged_attn_decode (the same
+ * kernels and split plan, so the outputs are identical bit for bit); the
+ * split partials go to a static device buffer of PKV_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends.  The
+ * call allocates and frees nothing.  A call whose split partials need more
+ * than that (paged_attn_decode_workspace_bytes(...) larger than
+ * PKV_NOALLOC_SCRATCH_BYTES) returns PKV_ERR_SCRATCH_TOO_SMALL and launches
+ * nothing.  Every call on one GPU shares that GPU's buffer: calls that may
+ * overlap in time (on different streams) race and must be serialised by the
+ * caller.  Nothing in the buffer needs clearing between calls: each call
+ * writes every partial it reads.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int paged_attn_decode_noalloc(const void* q, int q_dtype,
+                              const void* k_cache, const void* v_cache,
+                              const float* k_scales, const float* v_scales, int kv_dtype,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int max_context_len,
+                              int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                              int page_size, int num_pages, float scale, int window,
+                              void* out, int out_dtype, pkv_stream_t stream);
 
 /* Workspace bytes paged_attn_decode needs for these shapes (0 when the
  * contexts fit one partition, or for invalid shapes).  Pure host

@@ -34,7 +34,8 @@ class PkvError(RuntimeError):
 _lib = None
 
 
-ABI_VERSION = 2   # PKV_ABI_VERSION of include/pkv.h this binding marshals for
+ABI_VERSION = 3   # PKV_ABI_VERSION of include/pkv.h this binding marshals for
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                              _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_float, _c_int, _vp, _c_int, _vp,
                                              _c_size, _vp]
+    lib.paged_attn_decode_noalloc.restype = _c_int
+    lib.paged_attn_decode_noalloc.argtypes = [_vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int,
+                                              _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                              _c_int, _c_float, _c_int, _vp, _c_int, _vp]
     lib.paged_attn_decode_workspace_bytes.restype = _c_size
     lib.paged_attn_decode_workspace_bytes.argtypes = [_c_int] * 6
     lib.paged_attn_prefill_chunk.restype = _c_int
@@ -197,6 +202,21 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_conte
         _code(k_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
         int(max_context_len), B, hq, hkv, d, page, num_pages, float(scale), int(window),
         _ptr(out), _code(out), _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                              scale, out, k_scales=None, v_scales=None, stream=None, window=0):
+    """paged_attn_decode with its split partials in the library's static
+    device scratch: nothing is allocated (the caller passes `out`)."""
+    B, hq, d = q.shape
+    num_pages, hkv, page, _ = k_cache.shape
+    _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales)
+    _check("paged_attn_decode_noalloc", load_library().paged_attn_decode_noalloc(
+        _ptr(q), _code(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _code(k_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+        int(max_context_len), B, hq, hkv, d, page, num_pages, float(scale), int(window),
+        _ptr(out), _code(out), _stream(stream)))
     return out
 
 

@@ -11,6 +11,8 @@ extern "C" const char* pkv_status_string(int status) {
     case PKV_ERR_MISALIGNED: return "PKV_ERR_MISALIGNED: a tensor pointer is not 16-byte aligned";
     case PKV_ERR_WORKSPACE_TOO_SMALL: return "PKV_ERR_WORKSPACE_TOO_SMALL: workspace below the queried size";
     case PKV_ERR_HIP: return "PKV_ERR_HIP: a kernel launch failed";
+    case PKV_ERR_SCRATCH_TOO_SMALL:
+      return "PKV_ERR_SCRATCH_TOO_SMALL: the call needs more than the library's static scratch holds";
     default: return "PKV_ERR_UNKNOWN";
   }
 }

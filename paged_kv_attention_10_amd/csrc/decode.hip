@@ -44,6 +44,8 @@
 // converted exactly to fp16; the per-token K scale multiplies the score and
 // the per-token V scale folds into the probability.  fp32 KV uses the fp32
 // 16x16x4 MFMA.  exp is exp2 of a log2e-prescaled score.
+#include <mutex>
+
 #include "decode_body.h"
 
 namespace pkv {
@@ -235,4 +237,68 @@ extern "C" int paged_attn_decode_append(const void* q, int q_dtype, const void* 
                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                      num_kv_heads, head_dim, page_size, num_pages, scale, window, out, out_dtype,
                      workspace, workspace_bytes, k_new, v_new, new_dtype, stream);
+}
+
+// ------------------------------------------------ allocation-free decode
+// Split partials of paged_attn_decode_noalloc live in this file-scope device
+// array instead of a caller workspace.  Each GPU holds its own copy (at its
+// own address) from when the library's code is loaded on it until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: host code uses only the address hipGetSymbolAddress returns
+// for the device, looked up once per device and kept in g_scratch.
+constexpr size_t kNoAllocScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the device `stream` runs on (the
+// current device for the null stream), looked up with that device current
+// on the first call for it.
+int scratch_address(pkv_stream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return PKV_ERR_HIP;
+  int dev = cur;
+  if (stream && hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return PKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return PKV_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return PKV_ERR_HIP;
+    if (e != hipSuccess || !p) return PKV_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int paged_attn_decode_noalloc(const void* q, int q_dtype, const void* k_cache,
+                                         const void* v_cache, const float* k_scales,
+                                         const float* v_scales, int kv_dtype,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* context_lens, int max_context_len,
+                                         int batch, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int page_size, int num_pages, float scale,
+                                         int window, void* out, int out_dtype,
+                                         pkv_stream_t stream) {
+  // the split partials the plan needs (0 for shapes decode_call rejects)
+  const size_t need = paged_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads,
+                                                        head_dim, max_context_len, window);
+  if (need > kNoAllocScratchBytes) return PKV_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int st = scratch_address(stream, &ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_call(q, q_dtype, k_cache, v_cache, k_scales, v_scales, kv_dtype, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                     num_kv_heads, head_dim, page_size, num_pages, scale, window, out, out_dtype,
+                     ws, need > 0 ? kNoAllocScratchBytes : 0, nullptr, nullptr, PKV_F32, stream);
 }

@@ -24,7 +24,7 @@ def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert set(names) == {
         "pkv_abi_version", "pkv_status_string", "paged_kv_append", "paged_kv_append_rope",
-        "paged_attn_decode", "paged_attn_decode_append",
+        "paged_attn_decode", "paged_attn_decode_append", "paged_attn_decode_noalloc",
         "paged_attn_decode_workspace_bytes", "paged_attn_prefill_chunk",
         "paged_attn_prefill_workspace_bytes", "paged_attn_mixed", "paged_attn_mixed_workspace_bytes"}
     for n in names:
@@ -32,8 +32,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 2 == _lib.ABI_VERSION
-    for code in range(6):
+    assert lib.pkv_abi_version() == 3 == _lib.ABI_VERSION
+    for code in range(7):
         assert lib.pkv_status_string(code).decode().startswith("PKV_")
     assert lib.pkv_status_string(99).decode() == "PKV_ERR_UNKNOWN"
 
@@ -224,3 +224,36 @@ def _decode_append(lib, **over):
 ])
 def test_decode_append_rejects(lib, over, code):
     assert _decode_append(lib, **over) == code
+
+
+def _decode_noalloc(lib, **over):
+    a = dict(q=FAKE, qd=0, k=FAKE, v=FAKE, ks=None, vs=None, kvd=1, bt=FAKE, mb=8, cl=FAKE,
+             mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125, win=0, out=FAKE, od=0,
+             st=None)
+    a.update(over)
+    return lib.paged_attn_decode_noalloc(*a.values())
+
+
+SCRATCH_SMALL = 6
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, INVALID), ({"B": 0}, INVALID), ({"hq": 5}, INVALID), ({"sc": float("nan")}, INVALID),
+    ({"d": 96}, UNSUPPORTED), ({"out": FAKE + 2}, MISALIGNED),
+    # split partials beyond the static scratch: refused before any device call
+    ({"B": 1024, "hq": 32, "hkv": 8, "d": 128, "mcl": 262144, "mb": 16384}, SCRATCH_SMALL),
+])
+def test_decode_noalloc_rejects(lib, over, code):
+    assert _decode_noalloc(lib, **over) == code
+
+
+def test_noalloc_scratch_limit_matches_header(lib):
+    """The limit the binding states is the header's, and the refused shape
+    above does need more than it."""
+    text = open(_lib.HEADER).read()
+    assert "#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
+    assert _lib.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert lib.paged_attn_decode_workspace_bytes(1024, 32, 8, 128, 262144, 0) > _lib.NOALLOC_SCRATCH_BYTES
+    # the C2 decode shape fits
+    assert 0 < lib.paged_attn_decode_workspace_bytes(64, 12, 2, 128, 4096, 0) <= _lib.NOALLOC_SCRATCH_BYTES
