@@ -346,7 +346,9 @@ def ref_prefill_chunk(q, cache: PagedCache, block_tables, context_lens, cu_q_len
     """Chunked causal prefill.  q: [T, Hq, d]; sequence b's chunk is rows
     cu_q_lens[b]:cu_q_lens[b+1]; row i of it attends to [0, P_b + i] with
     P_b = context_lens[b] - C_b, or with a sliding window of `window` tokens
-    to (P_b + i - window, P_b + i].  Returns float64 [T, Hq, d]."""
+    to (P_b + i - window, P_b + i].  Positions a row does not attend take no
+    part in its sum, also when their V holds NaN or inf.  Returns float64
+    [T, Hq, d]."""
     q = np.asarray(q, dtype=np.float64)
     T, Hq, d = q.shape
     G = Hq // cache.num_kv_heads
@@ -364,13 +366,21 @@ def ref_prefill_chunk(q, cache: PagedCache, block_tables, context_lens, cu_q_len
         K, V = gather_sequence(cache, block_tables[b], n, lo)
         keypos = np.arange(lo, n)[None, :]
         rowpos = P + np.arange(C)[:, None]
+        seen = keypos <= rowpos
+        if window > 0:
+            seen = seen & (keypos > rowpos - window)
         for h in range(Hq):
             g = h // G
-            s = sc * (q[r0:r1, h, :] @ K[:, g, :].T)
-            s = np.where(keypos <= rowpos, s, -np.inf)
-            if window > 0:
-                s = np.where(keypos > rowpos - window, s, -np.inf)
-            out[r0:r1, h] = _softmax_rows(s) @ V[:, g, :]
+            s = np.where(seen, sc * (q[r0:r1, h, :] @ K[:, g, :].T), -np.inf)
+            w = _softmax_rows(s)
+            Vg = V[:, g, :]
+            if np.all(np.isfinite(Vg)):
+                out[r0:r1, h] = w @ Vg
+            else:
+                # a zero weight times a non-finite value would be NaN: sum
+                # each row over the positions it attends only
+                for i in range(C):
+                    out[r0 + i, h] = w[i, seen[i]] @ Vg[seen[i]]
     return out
 
 

@@ -293,6 +293,43 @@ def pin_chunk_split(O):
     assert np.max(np.abs(np.concatenate([a, b]) - full)) <= 1e-13
 
 
+def pin_prefill_unseen_nonfinite_v(O):
+    """A position a chunk row does not attend (after its causal limit, or
+    before its window) takes no part in that row, even when its V holds NaN
+    or inf: such rows equal the rows computed with that V finite, and the
+    rows that do attend it are non-finite in the heads of its KV head."""
+    import warnings
+    w = custom_workload(kind="prefill", context_lens=[40], q_lens=[24], num_q_heads=4,
+                        num_kv_heads=2, head_dim=8, seed=25)
+    P, p = 16, 16 + 9                       # rows 0..8 do not attend position p
+    c = _filled_cache(O, w)
+    clean = O.ref_prefill_chunk(w.q, c, w.block_tables, w.context_lens, w.cu_q_lens, w.scale)
+    page, off = int(w.block_tables[0, p // PS]), p % PS
+    for bad in (np.nan, np.inf):
+        c2 = _filled_cache(O, w)
+        c2.v[page, 1, 3, off] = bad          # KV head 1 serves query heads 2 and 3
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            out = O.ref_prefill_chunk(w.q, c2, w.block_tables, w.context_lens, w.cu_q_lens, w.scale)
+        assert np.max(np.abs(out[:p - P] - clean[:p - P])) <= 1e-13
+        assert np.all(~np.isfinite(out[p - P:, 2:, 3]))
+        assert np.array_equal(out[p - P:, :2], clean[p - P:, :2])
+    # a window of 4: row i attends (P+i-4, P+i], so rows from i = p-P+4 on
+    # no longer see p
+    c2 = _filled_cache(O, w)
+    c2.v[page, 1, 3, off] = np.nan
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        ref = O.ref_prefill_chunk(w.q, c, w.block_tables, w.context_lens, w.cu_q_lens, w.scale, window=4)
+        out = O.ref_prefill_chunk(w.q, c2, w.block_tables, w.context_lens, w.cu_q_lens, w.scale, window=4)
+    seen = [P + i - 4 < p <= P + i for i in range(24)]
+    for i in range(24):
+        if seen[i]:
+            assert np.all(np.isnan(out[i, 2:, 3]))
+        else:
+            assert np.max(np.abs(out[i] - ref[i])) <= 1e-13, i
+
+
 # ------------------------------------------------------------------ conversion pins
 def _golden_conv():
     with open(os.path.join(GOLDEN, "conversions.json")) as f:

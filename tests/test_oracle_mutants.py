@@ -16,8 +16,8 @@ SRC = inspect.getsource(O)
 MUTANTS = [
     ("gqa_map_modulo_decode", "            g = h // G\n            s = sc * (K[:, g, :] @ q[b, h])",
      "            g = h % cache.num_kv_heads\n            s = sc * (K[:, g, :] @ q[b, h])"),
-    ("gqa_map_modulo_prefill", "            g = h // G\n            s = sc * (q[r0:r1",
-     "            g = h % cache.num_kv_heads\n            s = sc * (q[r0:r1"),
+    ("gqa_map_modulo_prefill", "            g = h // G\n            s = np.where(seen, sc * (q[r0:r1",
+     "            g = h % cache.num_kv_heads\n            s = np.where(seen, sc * (q[r0:r1"),
     ("dropped_scale", "s = sc * (K[:, g, :] @ q[b, h])", "s = (K[:, g, :] @ q[b, h])"),
     ("causal_strict", "keypos <= rowpos", "keypos < rowpos"),
     ("causal_top_left", "rowpos = P + np.arange(C)[:, None]", "rowpos = np.arange(C)[:, None]"),
@@ -43,8 +43,9 @@ MUTANTS = [
      "lo = max(0, n - window - 1) if window > 0 else 0"),
     ("window_prefill_mask_inclusive", "keypos > rowpos - window", "keypos >= rowpos - window"),
     ("window_prefill_from_chunk_end", "keypos > rowpos - window", "keypos > P + C - 1 - window"),
-    ("window_prefill_mask_dropped", "            if window > 0:\n                s = np.where(",
-     "            if window < 0:\n                s = np.where("),
+    ("window_prefill_mask_dropped", "        if window > 0:\n            seen = seen &",
+     "        if window < 0:\n            seen = seen &"),
+    ("prefill_unseen_v_leaks", "            if np.all(np.isfinite(Vg)):", "            if True:"),
     ("window_prefill_first_key_late", "lo = max(0, P - window + 1) if window > 0 else 0",
      "lo = max(0, P - window + 2) if window > 0 else 0"),
     ("fp8_scale_240", "(absmax / np.float32(E4M3_MAX))", "(absmax / np.float32(240.0))"),
