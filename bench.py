@@ -315,41 +315,55 @@ def paged_overhead(g: Gpu, w, pool, decode_scattered, out_scattered, q, ws, step
             "pages": int(npg.sum())}
 
 
-def bench_prefill(g: Gpu, steps: int, warmup: int):
+PREFILL_VARIANTS = {
+    # name: (KV dtype, query dtype)
+    "C4": ("bf16", "bf16"),
+    "C4i8": ("i8", "bf16"),
+    "C4fp8": ("fp8", "bf16"),
+    "C4q32": ("bf16", "f32"),
+}
+
+
+def bench_prefill(g: Gpu, steps: int, warmup: int, name: str = "C4"):
+    """One step = the chunks' K/V appended + the prefill call, on C4's batch
+    with the KV cache and query dtypes of PREFILL_VARIANTS[name]."""
     from workloads import make_workload
+    kv, qd = PREFILL_VARIANTS[name]
     w = make_workload("C4")
-    log("[bench] C4: building the prefix pool on the GPU")
+    w.kv_dtype = kv
+    log(f"[bench] {name}: building the prefix pool on the GPU ({kv} KV, {qd} q)")
     pool = g.pool(w)
     new_rows = w.new_token_rows()
     old_mask = g.torch.ones(len(w.slot_mapping), dtype=g.torch.bool).numpy()
     old_mask[new_rows] = False
     g.fill_pool(w, pool, old_mask.nonzero()[0])
-    k, v, _, _ = pool
+    k, v, ks, vs = pool
     k_new, v_new = g.t(w.k[new_rows]), g.t(w.v[new_rows])
     slots_new = g.t(w.slot_mapping[new_rows])
-    q = g.t(w.q).to(g.torch.bfloat16)
+    q = g.t(w.q).to({"bf16": g.torch.bfloat16, "f32": g.torch.float32}[qd])
     bt, cl, cu = g.t(w.block_tables), g.t(w.context_lens), g.t(w.cu_q_lens)
     out = g.torch.empty((w.num_query_tokens, w.num_q_heads, w.head_dim), dtype=g.torch.float32,
                         device=g.dev)
 
     def prefill():
         g.pkv.paged_attn_prefill_chunk(q, k, v, bt, cl, cu, w.max_q_len, w.max_context_len,
-                                       w.scale, out=out)
+                                       w.scale, out=out, k_scales=ks, v_scales=vs)
 
     def step(inner, e1=None, e2=None):
-        g.pkv.paged_kv_append(k_new, v_new, slots_new, k, v)
+        g.pkv.paged_kv_append(k_new, v_new, slots_new, k, v, ks, vs)
         if e1 is not None:
             e1.record()
         inner()
         if e2 is not None:
             e2.record()
 
-    log(f"[bench] C4: {warmup} warmup + {steps} timed steps")
+    log(f"[bench] {name}: {warmup} warmup + {steps} timed steps")
     step_ms, inner_ms, wall = g.timed_steps(step, prefill, steps, warmup)
     flops = prefill_flops(w)
     st, si = stats(step_ms), stats(inner_ms)
     res = {
-        "workload": "C4", "desc": DESC["C4"], "algorithmic_flops": flops,
+        "workload": name, "desc": DESC["C4"], "kv_dtype": kv, "q_dtype": qd,
+        "algorithmic_flops": flops,
         "prefix_lens": w.meta["prefix_lens"].tolist(),
         "ms_per_step": st["mean"], "step_ms": st, "prefill_call_ms": si,
         "tflops_step": flops / (st["mean"] * 1e-3) / 1e12,
@@ -357,6 +371,13 @@ def bench_prefill(g: Gpu, steps: int, warmup: int):
         "prefill_tokens_per_s": w.num_query_tokens / (st["mean"] * 1e-3),
         "wall_s_timed_region": wall,
     }
+    if name != "C4":
+        # same peak (bf16 and fp16 dense MFMA: 2.5 PFLOP/s); counters are
+        # taken for the bf16 batch only
+        res["roofline"] = {"bound": "mfma", "achieved": res["tflops_prefill_call"],
+                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": res["tflops_prefill_call"] / BF16_PEAK_TFLOPS, "traffic": None}
+        return w, res, out
     res["roofline"] = {"bound": "mfma", "achieved": res["tflops_prefill_call"],
                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": res["tflops_prefill_call"] / BF16_PEAK_TFLOPS,
@@ -526,7 +547,8 @@ def main():
                     help="seconds of oracle CPU work for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of workloads to run (C1..C5, M1, M2, R1, W1, F1); default all")
+                    help="comma list of workloads to run (C1..C5, C4i8, C4fp8, C4q32, M1, M2, R1, "
+                         "W1, F1); default all")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -534,7 +556,7 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2", "R1",
-                                                        "W1", "F1"}
+                                                        "W1", "F1", "C4i8", "C4fp8", "C4q32"}
 
     g = Gpu()
     extras = {}
@@ -553,6 +575,10 @@ def main():
     if "C4" in only:
         _, rp, _ = bench_prefill(g, args.steps, args.warmup)
         extras["prefill_C4"] = rp
+    for name in ("C4i8", "C4fp8", "C4q32"):
+        if name in only:
+            _, rp, _ = bench_prefill(g, args.steps, args.warmup, name)
+            extras[f"prefill_{name}"] = rp
     for name in ("M1", "M2"):
         if name in only:
             extras[f"mixed_{name}"] = bench_mixed(g, name, args.steps, args.warmup)

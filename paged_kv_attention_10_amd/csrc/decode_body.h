@@ -58,9 +58,6 @@ __device__ __forceinline__ int checked_ctx(int raw, int max_ctx, int max_blocks,
   return raw;
 }
 
-// KV dtypes stored as one-byte codes with per-(token, head) scales.
-constexpr bool kv_code8(int kv) { return kv == PKV_I8 || kv == PKV_FP8; }
-
 template <int D, int KV>
 struct DecodeTile {
   // K fragments: 16-byte loads per MFMA row-half u.

@@ -24,17 +24,17 @@
 
 namespace pkv {
 
-template <int D>
+template <int D, int KV>
 constexpr int mixed_lds_bytes() {
-  return 2 * PrefillLds<D>::stage > DecodeSmem<D>::total ? 2 * PrefillLds<D>::stage
-                                                         : DecodeSmem<D>::total;
+  return 2 * PrefillLds<D, KV>::stage > DecodeSmem<D>::total ? 2 * PrefillLds<D, KV>::stage
+                                                             : DecodeSmem<D>::total;
 }
 
 static_assert(64 * kDecodeWaves == 256, "both kinds of workgroup have 256 threads");
 
 template <int D, int KV, bool QSPLIT>
 __global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs da, PrefillArgs pa, int n_prefill) {
-  __shared__ __attribute__((aligned(1024))) char lds[mixed_lds_bytes<D>()];
+  __shared__ __attribute__((aligned(1024))) char lds[mixed_lds_bytes<D, KV>()];
   const int id = blockIdx.x;
   if (id < n_prefill) {
     const int b = id % pa.batch, r = id / pa.batch;
@@ -51,7 +51,7 @@ template <int D, int KV>
 static void launch_mixed(const DecodeArgs& da, const PrefillArgs& pa, int n_prefill, int n_decode,
                          pkv_stream_t stream) {
   const dim3 grid(n_prefill + n_decode);
-  if (pa.q_dtype == KV)
+  if (!prefill_q_split(KV, pa.q_dtype))
     hipLaunchKernelGGL((mixed_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, da, pa,
                        n_prefill);
   else
@@ -65,8 +65,12 @@ static void launch_mixed(const DecodeArgs& da, const PrefillArgs& pa, int n_pref
 template <int D>
 static void dispatch_mixed(int kv, const DecodeArgs& da, const PrefillArgs& pa, int n_prefill,
                            int n_decode, pkv_stream_t stream) {
-  if (kv == PKV_BF16) launch_mixed<D, PKV_BF16>(da, pa, n_prefill, n_decode, stream);
-  else launch_mixed<D, PKV_F16>(da, pa, n_prefill, n_decode, stream);
+  switch (kv) {
+    case PKV_BF16: launch_mixed<D, PKV_BF16>(da, pa, n_prefill, n_decode, stream); break;
+    case PKV_F16: launch_mixed<D, PKV_F16>(da, pa, n_prefill, n_decode, stream); break;
+    case PKV_I8: launch_mixed<D, PKV_I8>(da, pa, n_prefill, n_decode, stream); break;
+    default: launch_mixed<D, PKV_FP8>(da, pa, n_prefill, n_decode, stream); break;
+  }
 }
 
 // Split plan of the one-token rows.  With long chunks in the batch
@@ -121,9 +125,10 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim) ||
       !decode_span_supported(max_context_len, window))
     return PKV_ERR_UNSUPPORTED;
-  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype == PKV_F32) return PKV_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      !aligned16(block_tables) || !aligned16(context_lens) || !aligned16(cu_q_lens))
+      !aligned16(block_tables) || !aligned16(context_lens) || !aligned16(cu_q_lens) ||
+      (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)))
     return PKV_ERR_MISALIGNED;
   if (num_tokens == 0 || max_q_len == 0) return PKV_OK;
 
@@ -136,8 +141,8 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   da.q = q;
   da.k_cache = k_cache;
   da.v_cache = v_cache;
-  da.k_scales = nullptr;
-  da.v_scales = nullptr;
+  da.k_scales = k_scales;
+  da.v_scales = v_scales;
   da.block_tables = block_tables;
   da.context_lens = context_lens;
   da.cu_q_lens = cu_q_lens;
@@ -167,6 +172,8 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   pa.q = q;
   pa.k_cache = k_cache;
   pa.v_cache = v_cache;
+  pa.k_scales = k_scales;
+  pa.v_scales = v_scales;
   pa.block_tables = block_tables;
   pa.context_lens = context_lens;
   pa.cu_q_lens = cu_q_lens;

@@ -25,6 +25,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kPage = PKV_PAGE_SIZE;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// KV dtypes stored as one-byte codes with per-(token, head) scales.
+constexpr bool kv_code8(int kv) { return kv == PKV_I8 || kv == PKV_FP8; }
+
 // ------------------------------------------------------------ conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
@@ -235,6 +238,26 @@ __device__ __forceinline__ void fp8x8_to_f16x8(u32x2 w, f16x8& out) {
     const uint32_t hi = __builtin_amdgcn_perm(0u, w[q], 0x030c020cu);   // codes 2, 3
     const f16x2 a = __builtin_bit_cast(f16x2, (lo & 0x80008000u) | ((lo >> 1) & 0x3f803f80u));
     const f16x2 b = __builtin_bit_cast(f16x2, (hi & 0x80008000u) | ((hi >> 1) & 0x3f803f80u));
+    out[4 * q + 0] = a[0];
+    out[4 * q + 1] = a[1];
+    out[4 * q + 2] = b[0];
+    out[4 * q + 3] = b[1];
+  }
+}
+
+// OCP FP8 E4M3 codes (4 per dword) -> fp16 holding the code's value:
+// gfx950's two-code convert to fp32 (v_cvt_pk_f32_fp8, which reads OCP
+// E4M3 on this chip: checked over all 256 codes, NaN codes giving NaN),
+// then a two-value pack to fp16, exact because every finite E4M3 value
+// (2^-9 .. 448) is an fp16 normal.
+__device__ __forceinline__ void fp8x8_to_f16x8_value(u32x2 w, f16x8& out) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], false);   // codes 0, 1
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], true);    // codes 2, 3
+    const f16x2 a = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(lo[0], lo[1]));
+    const f16x2 b = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(hi[0], hi[1]));
     out[4 * q + 0] = a[0];
     out[4 * q + 1] = a[1];
     out[4 * q + 2] = b[0];

@@ -15,6 +15,13 @@ inline bool head_dim_built(int d) { return d == 64 || d == 128; }
 inline bool io_dtype_ok(int dt) { return dt == PKV_F32 || dt == PKV_BF16 || dt == PKV_F16; }
 __host__ __device__ inline bool kv_scaled(int dt) { return dt == PKV_I8 || dt == PKV_FP8; }
 inline bool kv_dtype_ok(int dt) { return io_dtype_ok(dt) || kv_scaled(dt); }
+// Whether the prefill splits the query into head + remainder: a 16-bit
+// cache multiplies q in its own type (exact when q has that type), an
+// int8 / FP8 cache in fp16 (exact after a power-of-two row scaling for a
+// bf16 or fp16 q).
+inline bool prefill_q_split(int kv, int q_dtype) {
+  return kv_scaled(kv) ? q_dtype == PKV_F32 : q_dtype != kv;
+}
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 inline bool scale_ok(float scale) { return std::isfinite(scale); }
 

@@ -39,14 +39,18 @@
 // Precision: q and K/V in the cache's 16-bit type (an fp32 or other-typed
 // q is split into head + remainder and multiplied twice), P rounded to the
 // 16-bit type for PV (the normaliser sums those same rounded values, two
-// per packed dot product), fp32 accumulation.
+// per packed dot product), fp32 accumulation.  int8 / FP8 caches (Tiny-LLM
+// "Classifier receipt", KV cache point: INT8 or FP8 KV cache): codes
+// converted exactly to fp16 in registers, q scaled by a power of two and
+// rounded to fp16 (split for an fp32 q), the K scale on the score and the
+// V scale on the fp16 probability (prefill_body.h states the ranges).
 #include "prefill_body.h"
 
 namespace pkv {
 
 template <int D, int KV, bool QSPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * PrefillLds<D>::stage];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * PrefillLds<D, KV>::stage];
   int b = blockIdx.x, g = blockIdx.y;
   int rb = a.nrowblocks - 1 - (int)blockIdx.z;   // heavier (later) row blocks first
   const long id = blockIdx.x + (long)a.batch * (blockIdx.y + (long)a.hkv * blockIdx.z);
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 template <int D, int KV>
 static void dispatch_prefill_q(const PrefillArgs& a, pkv_stream_t stream) {
   dim3 grid(a.batch, a.hkv, a.nrowblocks);
-  if (a.q_dtype == KV)
+  if (!prefill_q_split(KV, a.q_dtype))
     hipLaunchKernelGGL((prefill_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
   else
     hipLaunchKernelGGL((prefill_kernel<D, KV, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
@@ -66,8 +70,12 @@ static void dispatch_prefill_q(const PrefillArgs& a, pkv_stream_t stream) {
 
 template <int D>
 static void dispatch_prefill(int kv, const PrefillArgs& a, pkv_stream_t stream) {
-  if (kv == PKV_BF16) dispatch_prefill_q<D, PKV_BF16>(a, stream);
-  else dispatch_prefill_q<D, PKV_F16>(a, stream);
+  switch (kv) {
+    case PKV_BF16: dispatch_prefill_q<D, PKV_BF16>(a, stream); break;
+    case PKV_F16: dispatch_prefill_q<D, PKV_F16>(a, stream); break;
+    case PKV_I8: dispatch_prefill_q<D, PKV_I8>(a, stream); break;
+    default: dispatch_prefill_q<D, PKV_FP8>(a, stream); break;
+  }
 }
 
 }  // namespace pkv
@@ -106,9 +114,10 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
   if (kv_scaled(kv_dtype) != (k_scales != nullptr) || kv_scaled(kv_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim)) return PKV_ERR_UNSUPPORTED;
-  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype == PKV_F32) return PKV_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      !aligned16(block_tables) || !aligned16(context_lens) || !aligned16(cu_q_lens))
+      !aligned16(block_tables) || !aligned16(context_lens) || !aligned16(cu_q_lens) ||
+      (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)))
     return PKV_ERR_MISALIGNED;
   if (num_tokens == 0 || max_q_len == 0) return PKV_OK;
 
@@ -116,6 +125,8 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.cu_q_lens = cu_q_lens;

@@ -38,6 +38,8 @@ struct PrefillArgs {
   const void* q;
   const void* k_cache;
   const void* v_cache;
+  const float* k_scales;   // int8 / FP8 caches only
+  const float* v_scales;
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* cu_q_lens;
@@ -56,14 +58,17 @@ struct PrefillArgs {
   int window;        // sliding window in tokens, 0 = the whole causal prefix
 };
 
-template <int D>
+// One tile stage in LDS: four pages of K rows, then four V^T page blocks,
+// then (int8 / FP8) each page's 16 K scales and 16 V scales.
+template <int D, int KV>
 struct PrefillLds {
-  static constexpr int kRow = 2 * D;                 // bytes of one K row
+  static constexpr int ES = kv_code8(KV) ? 1 : 2;    // bytes per cached element
+  static constexpr int kRow = ES * D;                // bytes of one K row
   static constexpr int kPageBytes = kPage * kRow;    // one page of K (= one page of V^T)
   static constexpr int vOff = 4 * kPageBytes;        // V^T blocks after the 64 K rows
-  static constexpr int stage = 8 * kPageBytes;
+  static constexpr int sOff = 8 * kPageBytes;        // per page: 16 K scales, 16 V scales
+  static constexpr int stage = 8 * kPageBytes + (kv_code8(KV) ? 4 * 128 : 0);
   static constexpr int dmaPerPage = kPageBytes / 1024;
-  static constexpr int chunksPerRow = D / 8;
 };
 
 // 16-byte-chunk swizzle of K row rr (its offset in the page): chunk c of the
@@ -72,6 +77,16 @@ template <int D>
 __device__ __forceinline__ int k_swizzle(int rr) {
   if constexpr (D == 128) return (rr ^ ((rr & 8) >> 1)) & 15;
   else return (rr ^ (rr >> 3)) & 7;
+}
+
+// The same for one-byte K rows (D bytes), which also depends on the parity
+// p of the page in the tile: a 16-lane fragment read touches rows 0-7 or
+// 8-15 of two neighbouring pages, and these slots put its 16 chunks in 16
+// different 16-byte bank slots (and any 8 lanes of it in 8 of 128 bytes).
+template <int D>
+__device__ __forceinline__ int k_swizzle8(int p, int rr) {
+  if constexpr (D == 128) return ((rr ^ (rr >> 2)) & 3) | (p << 2);
+  else return (((rr >> 1) ^ (rr >> 2)) & 1) | (p << 1);
 }
 
 constexpr float kLazyRescale = 8.0f;
@@ -155,15 +170,51 @@ __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int* sh, long
   return true;
 }
 
+// x * y with 0 * anything = 0 (NaN and inf included): v_mul_legacy_f32,
+// reached through its LLVM intrinsic (not inline asm, so that the compiler
+// sees the instruction and keeps the wait states it needs, e.g. after a
+// transcendental that produced x).
+extern "C" __device__ float pkv_fmul_legacy(float, float) __asm("llvm.amdgcn.fmul.legacy");
+__device__ __forceinline__ float mul_zero_wins(float x, float y) { return pkv_fmul_legacy(x, y); }
+
+// int8 / FP8 codes (8 per 64 bits) -> fp16 values, exact.
+template <int KV>
+__device__ __forceinline__ f16x8 codes8_to_f16(u32x2 w) {
+  f16x8 r;
+  if constexpr (KV == PKV_FP8) fp8x8_to_f16x8_value(w, r);
+  else i8x8_to_f16x8(w, r);
+  return r;
+}
+
 // One row block: the 128 rows rb of (sequence b, KV head g).  Called by all
 // 256 threads of the workgroup; `lds` holds two tile stages (1024-aligned).
+//
+// int8 / FP8 caches: the tile's codes and scales are copied as they lie and
+// each wave converts the codes it reads to fp16, exactly (int8 with the
+// v_perm + subtract trick, FP8 with the hardware convert).  The query row is
+// scaled by the power of two 2^e that puts its largest magnitude in
+// [2^14, 2^15) and rounded to fp16 (split into head + remainder for an fp32
+// query); a bf16 or fp16 query is then exact down to 2^-32 of that largest
+// magnitude.  The scores take the K scale and c * 2^-e.  The V scale
+// multiplies the probability (0 * anything = 0 there, so a NaN scale of a
+// masked key stays out), normalised per wave as in the decode: scales are
+// multiplied by 2^(4 - v_exp), v_exp the binade of the largest in-range
+// scale met so far, raised (with the accumulator scaled down to match) when
+// a tile's largest scale lies more than two binades above it, so p * scale
+// stays below 2^14 in fp16; the power of two goes back on at the end.  The
+// A-operand row of S^T reads another key than in the 16-bit case: lane
+// (c + 32*h) then holds, for query row c, the scores of all 16 keys of page
+// 2*hf + h of the tile (register r: key r), so one 16-byte V^T read covers
+// both PV k-steps of a half and a lane's scales are one page's.
 template <int D, int KV, bool QSPLIT>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, int b, int g, int rb) {
+  constexpr bool kI8 = kv_code8(KV);
   constexpr bool kBF16 = (KV == PKV_BF16);
   using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
-  using L = PrefillLds<D>;
+  using L = PrefillLds<D, KV>;
   constexpr int NSTEP = D / 16;  // QK k-steps of 16
   constexpr int NDB = D / 32;    // 32-row blocks of d for PV
+  constexpr int KCH = D / 32;    // one-byte K: 16-byte chunks per lane and half
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -207,9 +258,19 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   const int npages = (ctx + kPage - 1) / kPage;
   const long qrow = ((long)(q0 + pos) * a.hq + h) * D;
 
-  // ---- Q^T fragments (B operand): column col, k-chunk d = 16*s + 8*hh
+  // ---- Q^T fragments (B operand), column col.  16-bit caches: k-chunk
+  //      d = 16*s + 8*hh; one-byte caches: d = (D/2)*hh + 8*s, so that a
+  //      lane's K codes for its k-steps are one contiguous run of its row.
+  //      A query in the cache's own 16-bit type is used as it is; otherwise
+  //      the row goes through fp32 (times the sign of the scale) and, when
+  //      the MFMA takes fp16, is scaled by the power of two 2^e that puts its
+  //      largest magnitude in [2^14, 2^15) (fp16's range then holds it, and
+  //      a bf16 or fp16 row is exact down to 2^-32 of that magnitude); it is
+  //      rounded to the MFMA type, split into head + remainder for an fp32
+  //      or other-typed query, and the scores take c * 2^-e.
   H8 qhi[NSTEP], qlo[QSPLIT ? NSTEP : 1];
-  if constexpr (!QSPLIT) {
+  float row_c = a.scale_log2;   // c * 2^-e for this row
+  if constexpr (!kI8 && !QSPLIT) {
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       const int d0 = 16 * s + 8 * hh;
@@ -224,20 +285,42 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
       constexpr int QT = decltype(qdt)::value;
       uint32_t bits[NSTEP][8];
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) io_bits_vec<8, QT>(a.q, qrow + 16 * s + 8 * hh, bits[s]);
+      for (int s = 0; s < NSTEP; ++s)
+        io_bits_vec<8, QT>(a.q, qrow + (kI8 ? (D / 2) * hh + 8 * s : 16 * s + 8 * hh), bits[s]);
+      float x[NSTEP][8];
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[s][i] = live ? io_value<QT>(bits[s][i]) * a.q_mul : 0.f;
+      if constexpr (!kBF16) {
+        uint32_t amk = 0;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) amk = max(amk, abs_key(x[s][i]));
+        amk = max(amk, (uint32_t)__shfl_xor((int)amk, 32));
+        const float am = __uint_as_float(amk);
+        // zero, inf or NaN rows keep e = 0
+        const int e = (am > 0.f && am <= 3.402823466e38f) ? 15 - __builtin_amdgcn_frexp_expf(am) : 0;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[s][i] = __builtin_ldexpf(x[s][i], e);
+        row_c = __builtin_ldexpf(a.scale_log2, -e);
+      }
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
-        float x[8];
+        if constexpr (QSPLIT && kBF16) {
+          const auto sp = split_bf16(x[s]);
+          qhi[s] = sp.hi;
+          qlo[s] = sp.lo;
+        } else if constexpr (QSPLIT) {
+          const auto sp = split_f16(x[s]);
+          qhi[s] = sp.hi;
+          qlo[s] = sp.lo;
+        } else if constexpr (!kBF16) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? io_value<QT>(bits[s][e]) * a.q_mul : 0.f;
-        if constexpr (kBF16) {
-          auto sp = split_bf16(x);
-          qhi[s] = sp.hi;
-          qlo[s] = sp.lo;
-        } else {
-          auto sp = split_f16(x);
-          qhi[s] = sp.hi;
-          qlo[s] = sp.lo;
+          for (int i = 0; i < 8; ++i) qhi[s][i] = (_Float16)x[s][i];
         }
       }
     });
@@ -254,8 +337,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   int pid_next = ntiles > (t_first | 15) + 1 ? load_window((t_first >> 4) + 1) : 0;
 
   // ---- tile copy: wave w moves page 4t + w of the tile (K rows swizzled,
-  //      V^T block as is) into stage `stg`; pages past the context are not
-  //      read (their keys are masked and their V is zeroed in registers)
+  //      V^T block as is, and for one-byte caches the page's 16 K and 16 V
+  //      scales, lanes 0-3 and 4-7) into stage `stg`; pages past the context
+  //      are not read (their keys are masked and their V is zeroed or
+  //      weighted by zero)
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
   int koff[L::dmaPerPage];
@@ -263,8 +348,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   for (int j = 0; j < L::dmaPerPage; ++j) {
     const int byte = 1024 * j + 16 * lane;          // position inside the page's K block
     const int rr = byte / L::kRow, slot = (byte % L::kRow) / 16;
-    koff[j] = rr * L::kRow + ((slot ^ k_swizzle<D>(rr)) * 16);
+    if constexpr (kI8) koff[j] = rr * L::kRow + ((slot ^ k_swizzle8<D>(wave & 1, rr)) * 16);
+    else koff[j] = rr * L::kRow + ((slot ^ k_swizzle<D>(rr)) * 16);
   }
+  const char* sc_src = nullptr;
+  if constexpr (kI8)
+    sc_src = reinterpret_cast<const char*>(lane < 4 ? a.k_scales : a.v_scales) + 16 * (lane & 3);
   auto issue_tile = [&](int t, int stg) {
     if ((t & 15) == 0 && t > t_first) {
       pid_cur = pid_next;
@@ -282,155 +371,311 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         dma16(kc + blk + koff[j], lk + 1024 * j);
         dma16(vc + blk + 1024 * j + 16 * lane, lv + 1024 * j);
       }
+      if constexpr (kI8) {
+        if (lane < 8)
+          dma16(sc_src + ((long)pid * a.hkv + g) * (kPage * 4), lds + stg * L::stage + L::sOff + 128 * wave);
+      }
     }
   };
-
-  // per-lane LDS offsets of the fragment reads
-  const int krow = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
-  int kaddr[NSTEP];
-#pragma unroll
-  for (int k = 0; k < NSTEP; ++k)
-    kaddr[k] = krow * L::kRow + (((2 * k + hh) ^ k_swizzle<D>(krow & 15)) * 16);
-  const int vaddr = L::vOff + col * 32 + hh * 16;
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
   float m_run = -INFINITY;
   float l_part = 0.f;
+  int v_exp = -1000;   // one-byte caches: acc holds the output times 2^-(v_exp - 4)
 
-  // one 64-key tile (keys kb .. kb+63; half hf = pages 2hf and 2hf+1)
-  auto compute_tile = [&](const char* st, int kb) {
-    // ---- S^T = K * Q^T for both halves: all K fragment reads first (one
-    //      LDS latency), then two independent MFMA chains
-    u32x4 kfr[2][NSTEP];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int k = 0; k < NSTEP; ++k)
-        kfr[hf][k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kaddr[k]);
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  // ---- pipeline: tile t computes from LDS while tile t+1 is copied in
+  auto run_tiles = [&](auto&& compute_tile) {
+    issue_tile(t_first, t_first & 1);
+    __syncthreads();  // waits for this wave's copies, then for every wave's
+    for (int t = t_first; t < ntiles; ++t) {
+      if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
+      const char* st = lds + (t & 1) * L::stage;
+      const int kb = t * kPrefillTileKeys;
+      // every wave computes every tile: a tile past all of a wave's rows is
+      // fully masked (p = 0), and branching around it would make the compiler
+      // copy the accumulators at each join
+      compute_tile(st, kb);
+      __syncthreads();
+    }
+  };
+
+  if constexpr (!kI8) {
+    // per-lane LDS offsets of the fragment reads
+    const int krow = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
+    int kaddr[NSTEP];
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const H8 kf = __builtin_bit_cast(H8, kfr[hf][k]);
-        s[hf] = mfma32x32x16(kf, qhi[k], s[hf]);
-        if constexpr (QSPLIT) s[hf] = mfma32x32x16(kf, qlo[k], s[hf]);
-      }
-    // keep the K reads ahead of the MFMAs (the default schedule pairs them
-    // and waits for LDS between every two MFMAs)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NSTEP, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, (QSPLIT ? 4 : 2) * NSTEP, 0);
-    // ---- V^T fragments (their LDS latency hides behind the softmax)
-    u32x4 vfr[2][NDB][2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          vfr[hf][db][j] = *reinterpret_cast<const u32x4*>(
-              st + vaddr + (2 * hf + j) * L::kPageBytes + db * 32 * 32);
-    // keys at or past the context end, or in pages not read because they
-    // lie wholly before the window, may hold anything: zero their V
-    if (kb + 64 > ctx || kb < kPage * p_first) {
+      kaddr[k] = krow * L::kRow + (((2 * k + hh) ^ k_swizzle<D>(krow & 15)) * 16);
+    const int vaddr = L::vOff + col * 32 + hh * 16;
+
+    // one 64-key tile (keys kb .. kb+63; half hf = pages 2hf and 2hf+1)
+    run_tiles([&](const char* st, int kb) {
+      // ---- S^T = K * Q^T for both halves: all K fragment reads first (one
+      //      LDS latency), then two independent MFMA chains
+      u32x4 kfr[2][NSTEP];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int key0 = kb + 32 * hf + 16 * j + 8 * hh;
+        for (int k = 0; k < NSTEP; ++k)
+          kfr[hf][k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kaddr[k]);
+      f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const bool out = key0 + e >= ctx || key0 + e < kPage * p_first;
-            const uint32_t m = out ? ((e & 1) ? 0x0000ffffu : 0xffff0000u) : 0xffffffffu;
+      for (int k = 0; k < NSTEP; ++k)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) vfr[hf][db][j][e >> 1] &= m;
-          }
+        for (int hf = 0; hf < 2; ++hf) {
+          const H8 kf = __builtin_bit_cast(H8, kfr[hf][k]);
+          s[hf] = mfma32x32x16(kf, qhi[k], s[hf]);
+          if constexpr (QSPLIT) s[hf] = mfma32x32x16(kf, qlo[k], s[hf]);
         }
-    }
-    // ---- online softmax for query row `col`; register r of half hf holds
-    //      key kb + 32*hf + 16*(r/8) + 8*hh + r%8, masked when that exceeds
-    //      `limit`.  Raw scores are masked and maximised; the log2e-prescaled
-    //      scale (positive) is applied inside the exponent: p = 2^(s*c - m).
-    if (kb + 63 > lim_min) {
+      // keep the K reads ahead of the MFMAs (the default schedule pairs them
+      // and waits for LDS between every two MFMAs)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NSTEP, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (QSPLIT ? 4 : 2) * NSTEP, 0);
+      // ---- V^T fragments (their LDS latency hides behind the softmax)
+      u32x4 vfr[2][NDB][2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int rel = limit - (kb + 32 * hf + 8 * hh);   // largest allowed 16*(r/8) + r%8
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (16 * (r >> 3) + (r & 7) > rel) s[hf][r] = -INFINITY;
-      }
-    }
-    if (kb < win_max) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int rel = wlo - (kb + 32 * hf + 8 * hh);     // smallest allowed 16*(r/8) + r%8
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (16 * (r >> 3) + (r & 7) < rel) s[hf][r] = -INFINITY;
-      }
-    }
-    float mt = s[0][0];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
-    mt = max_xor32(mt) * a.scale_log2;
-    const bool grow = mt > m_run + kLazyRescale;
-    if (__any(grow)) {
-      const float m_new = grow ? mt : m_run;
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float lsum = 0.f;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      H8 p16[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][r], a.scale_log2, -m_use));
-        if constexpr (kBF16) p16[r >> 3][r & 7] = (__bf16)p;
-        else p16[r >> 3][r & 7] = (_Float16)p;
-      }
-      // the row sum takes the rounded probabilities the PV multiplies, two
-      // per packed dot product with (1, 1)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        if constexpr (kBF16) {
-          const bf16x2 pair = {p16[r >> 3][r & 7], p16[r >> 3][(r & 7) + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.f, (__bf16)1.f}, lsum, false);
-        } else {
-          const f16x2 pair = {p16[r >> 3][r & 7], p16[r >> 3][(r & 7) + 1]};
-          lsum = __builtin_amdgcn_fdot2(pair, f16x2{(_Float16)1.f, (_Float16)1.f}, lsum, false);
-        }
-      }
-      // ---- O^T += V^T * P^T
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[hf][db][j]), p16[j], acc[db]);
-    }
-    l_part += lsum;
-  };
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            vfr[hf][db][j] = *reinterpret_cast<const u32x4*>(
+                st + vaddr + (2 * hf + j) * L::kPageBytes + db * 32 * 32);
+      // keys at or past the context end, or in pages not read because they
+      // lie wholly before the window, may hold anything: zero their V
+      if (kb + 64 > ctx || kb < kPage * p_first) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int key0 = kb + 32 * hf + 16 * j + 8 * hh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const bool out = key0 + e >= ctx || key0 + e < kPage * p_first;
+              const uint32_t m = out ? ((e & 1) ? 0x0000ffffu : 0xffff0000u) : 0xffffffffu;
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) vfr[hf][db][j][e >> 1] &= m;
+            }
+          }
+      }
+      // ---- online softmax for query row `col`; register r of half hf holds
+      //      key kb + 32*hf + 16*(r/8) + 8*hh + r%8, masked when that exceeds
+      //      `limit`.  Raw scores are masked and maximised; the log2e-prescaled
+      //      scale (positive) is applied inside the exponent: p = 2^(s*c - m).
+      if (kb + 63 > lim_min) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int rel = limit - (kb + 32 * hf + 8 * hh);   // largest allowed 16*(r/8) + r%8
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (16 * (r >> 3) + (r & 7) > rel) s[hf][r] = -INFINITY;
+        }
+      }
+      if (kb < win_max) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int rel = wlo - (kb + 32 * hf + 8 * hh);     // smallest allowed 16*(r/8) + r%8
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (16 * (r >> 3) + (r & 7) < rel) s[hf][r] = -INFINITY;
+        }
+      }
+      float mt = s[0][0];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
+      mt = max_xor32(mt) * row_c;
+      const bool grow = mt > m_run + kLazyRescale;
+      if (__any(grow)) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float lsum = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        H8 p16[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][r], row_c, -m_use));
+          if constexpr (kBF16) p16[r >> 3][r & 7] = (__bf16)p;
+          else p16[r >> 3][r & 7] = (_Float16)p;
+        }
+        // the row sum takes the rounded probabilities the PV multiplies, two
+        // per packed dot product with (1, 1)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          if constexpr (kBF16) {
+            const bf16x2 pair = {p16[r >> 3][r & 7], p16[r >> 3][(r & 7) + 1]};
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.f, (__bf16)1.f}, lsum, false);
+          } else {
+            const f16x2 pair = {p16[r >> 3][r & 7], p16[r >> 3][(r & 7) + 1]};
+            lsum = __builtin_amdgcn_fdot2(pair, f16x2{(_Float16)1.f, (_Float16)1.f}, lsum, false);
+          }
+        }
+        // ---- O^T += V^T * P^T
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[hf][db][j]), p16[j], acc[db]);
+      }
+      l_part += lsum;
+    });
+  } else {
+    // per-lane LDS offsets: the A-operand row col of S^T reads key
+    // 16*((col/4)&1) + 4*(col/8) + col%4 of the half (page (col/4)&1), its
+    // k-chunks (D/32)*hh .. (D/32)*hh + D/32 - 1; V^T row d = col of the
+    // half's page hh (+ 32*db)
+    const int key = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+    const int kp = key >> 4, krr = key & 15;
+    int kaddr[KCH];
+#pragma unroll
+    for (int i = 0; i < KCH; ++i)
+      kaddr[i] = kp * L::kPageBytes + krr * L::kRow + ((((D / 32) * hh + i) ^ k_swizzle8<D>(kp, krr)) * 16);
+    const int vaddr = L::vOff + hh * L::kPageBytes + col * 16;
+    const int saddr = L::sOff + 128 * hh;
 
-  // ---- pipeline: tile t computes from LDS while tile t+1 is copied in
-  issue_tile(t_first, t_first & 1);
-  __syncthreads();  // waits for this wave's copies, then for every wave's
-  for (int t = t_first; t < ntiles; ++t) {
-    if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
-    const char* st = lds + (t & 1) * L::stage;
-    const int kb = t * kPrefillTileKeys;
-    // every wave computes every tile: a tile past all of a wave's rows is
-    // fully masked (p = 0), and branching around it would make the compiler
-    // copy the accumulators at each join
-    compute_tile(st, kb);
-    __syncthreads();
+    run_tiles([&](const char* st, int kb) {
+      // ---- S^T = K * Q^T: the lane's K chunks of both halves, then the MFMAs
+      u32x4 kfr[2][KCH];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < KCH; ++i)
+          kfr[hf][i] = *reinterpret_cast<const u32x4*>(st + hf * 2 * L::kPageBytes + kaddr[i]);
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int k = 0; k < NSTEP; ++k)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const u32x4 w = kfr[hf][k >> 1];
+          const u32x2 codes = (k & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+          const f16x8 kf = codes8_to_f16<KV>(codes);
+          s[hf] = mfma32x32x16(kf, qhi[k], s[hf]);
+          if constexpr (QSPLIT) s[hf] = mfma32x32x16(kf, qlo[k], s[hf]);
+        }
+      // ---- V^T codes (16 keys of one d row of the lane's page per half)
+      //      and that page's scales
+      u32x4 vfr[2][NDB];
+      f32x4 ksc[2][4], vsc[2][4];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          vfr[hf][db] = *reinterpret_cast<const u32x4*>(st + vaddr + hf * 2 * L::kPageBytes + db * 32 * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ksc[hf][i] = *reinterpret_cast<const f32x4*>(st + saddr + 256 * hf + 16 * i);
+          vsc[hf][i] = *reinterpret_cast<const f32x4*>(st + saddr + 256 * hf + 64 + 16 * i);
+        }
+      }
+      // ---- scores in log2 units; register r of half hf holds key
+      //      kb + 32*hf + 16*hh + r, masked past `limit` and before `wlo`
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[hf][r] *= ksc[hf][r >> 2][r & 3] * row_c;
+      if (kb + 63 > lim_min) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int rel = limit - (kb + 32 * hf + 16 * hh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r > rel) s[hf][r] = -INFINITY;
+        }
+      }
+      if (kb < win_max) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int rel = wlo - (kb + 32 * hf + 16 * hh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r < rel) s[hf][r] = -INFINITY;
+        }
+      }
+      float mt = s[0][0];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
+      mt = max_xor32(mt);
+      const bool grow = mt > m_run + kLazyRescale;
+      if (__any(grow)) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      // ---- V scales: keys at or past the context end, or in pages not read,
+      //      may hold anything (scales and, for FP8, NaN codes): their scale
+      //      is taken as 0 and their codes zeroed
+      const bool edge = kb + 64 > ctx || kb < kPage * p_first;
+      float vs[2][16];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int key0 = kb + 32 * hf + 16 * hh;
+        const int nv = key0 < kPage * p_first ? 0 : ctx - key0;   // in-range keys of the page
+#pragma unroll
+        for (int r = 0; r < 16; ++r) vs[hf][r] = (!edge || r < nv) ? vsc[hf][r >> 2][r & 3] : 0.f;
+        if constexpr (KV == PKV_FP8) {
+          if (edge) {
+            u32x4 m;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int n = min(max(nv - 4 * q, 0), 4);
+              m[q] = n >= 4 ? 0xffffffffu : ((1u << (8 * n)) - 1u);
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) vfr[hf][db] &= m;
+          }
+        }
+      }
+      float vmax = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, vs[hf][r]);
+      vmax = max_xor32(vmax);
+      const int et = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(vmax));
+      if (et > v_exp + 2) {
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][r] = __builtin_ldexpf(acc[i][r], v_exp - et);
+        v_exp = et;
+      }
+      float lsum = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f16x8 p16[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[hf][r] - m_use);
+          lsum += p;
+          p16[r >> 3][r & 7] = (_Float16)mul_zero_wins(p, __builtin_ldexpf(vs[hf][r], 4 - v_exp));
+        }
+        // ---- O^T += V^T * P^T: keys 0-7 of the page, then 8-15
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const f16x8 v0 = codes8_to_f16<KV>(u32x2{vfr[hf][db][0], vfr[hf][db][1]});
+          const f16x8 v1 = codes8_to_f16<KV>(u32x2{vfr[hf][db][2], vfr[hf][db][3]});
+          acc[db] = mfma32x32x16(v0, p16[0], acc[db]);
+          acc[db] = mfma32x32x16(v1, p16[1], acc[db]);
+        }
+      }
+      l_part += lsum;
+    });
   }
   bad = __syncthreads_or(bad);
 
@@ -438,6 +683,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   if (!live) return;
   // a NaN score makes the row sum NaN while the max skips it: NaN, not zero
   const float inv = (bad || l_run != l_run) ? NAN : (l_run > 0.f ? 1.f / l_run : 0.f);
+  const int o_exp = v_exp - 4;   // one-byte caches
   const long orow = ((long)(q0 + pos) * a.hq + h) * D;
   // lane (col + 32*hh), register r of block db holds d = 32*db + 8*(r/4) + 4*hh + r%4:
   // four consecutive d per group of four registers
@@ -450,6 +696,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         const long o = orow + 32 * db + 8 * r4 + 4 * hh;
         f32x4 v = {acc[db][4 * r4] * inv, acc[db][4 * r4 + 1] * inv, acc[db][4 * r4 + 2] * inv,
                    acc[db][4 * r4 + 3] * inv};
+        if constexpr (kI8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __builtin_ldexpf(v[e], o_exp);
+        }
         if constexpr (std::is_same<T, float>::value) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = v;
         } else {

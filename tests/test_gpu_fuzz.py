@@ -54,11 +54,11 @@ def test_decode_fuzz(pkv, it):
     assert err <= TOL[kv], err
 
 
-@pytest.mark.parametrize("it", range(12))
+@pytest.mark.parametrize("it", range(16))
 def test_prefill_fuzz(pkv, it):
     rng = np.random.default_rng(3000 + it)
-    kv = ["bf16", "f16"][it % 2]
-    d = [64, 128][(it // 2) % 2]
+    kv = ["bf16", "f16", "i8", "fp8"][it % 4]
+    d = [64, 128][(it // 4) % 2]
     hkv = int(rng.choice([1, 2]))
     G = int(rng.choice([1, 3, 6, 8]))
     B = int(rng.integers(1, 6))
@@ -69,7 +69,7 @@ def test_prefill_fuzz(pkv, it):
     say(f"prefill fuzz {it}: kv={kv} d={d} Hkv={hkv} G={G} P={prefix} C={chunk}")
     cache = oracle_cache(w)
     gc = poisoned_gpu_cache(cache, used_slot_mask(w))
-    q = q_tensor(w, kv)
+    q = q_tensor(w, kv if kv in ("bf16", "f16") else ["bf16", "f16", "f32"][it % 3])
     out = run_prefill(pkv, w, gc, q)
     assert out.shape == q.shape
     if w.num_query_tokens == 0:            # every chunk empty: a no-op

@@ -94,13 +94,14 @@ def test_decode_window_covering_context_is_plain_decode(pkv):
 def _prefill(pkv, fn, w, gc, q, bt, window):
     out = getattr(pkv, fn)(q, gc["k"], gc["v"], np_to_gpu(bt), np_to_gpu(w.context_lens),
                            np_to_gpu(w.cu_q_lens), w.max_q_len, w.max_context_len, w.scale,
-                           window=window)
+                           k_scales=gc["ks"], v_scales=gc["vs"], window=window)
     torch.cuda.synchronize()
     return out
 
 
 @pytest.mark.parametrize("fn", ["paged_attn_prefill_chunk", "paged_attn_mixed"])
-@pytest.mark.parametrize("kv,d,qd", [("bf16", 128, "bf16"), ("f16", 64, "f32")])
+@pytest.mark.parametrize("kv,d,qd", [("bf16", 128, "bf16"), ("f16", 64, "f32"), ("i8", 128, "bf16"),
+                                     ("fp8", 64, "f16")])
 @pytest.mark.parametrize("window", [1, 5, 64, 100, 300, 1000])
 def test_prefill_window(pkv, fn, kv, d, qd, window):
     say(f"{fn} window={window} kv={kv} d={d} q={qd}")
