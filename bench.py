@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
 ELEM = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "fp8": 1}
 DESC = {
     "C1": "paged decode, fp32 q/KV/out, batch 4, 9 q / 3 KV heads, head_dim 64, ctx {17,64,133,200}",
@@ -321,6 +322,7 @@ PREFILL_VARIANTS = {
     "C4i8": ("i8", "bf16"),
     "C4fp8": ("fp8", "bf16"),
     "C4q32": ("bf16", "f32"),
+    "C4f32": ("f32", "f32"),
 }
 
 
@@ -341,6 +343,7 @@ def bench_prefill(g: Gpu, steps: int, warmup: int, name: str = "C4"):
     k_new, v_new = g.t(w.k[new_rows]), g.t(w.v[new_rows])
     slots_new = g.t(w.slot_mapping[new_rows])
     q = g.t(w.q).to({"bf16": g.torch.bfloat16, "f32": g.torch.float32}[qd])
+    peak = FP32_PEAK_TFLOPS if kv == "f32" else BF16_PEAK_TFLOPS
     bt, cl, cu = g.t(w.block_tables), g.t(w.context_lens), g.t(w.cu_q_lens)
     out = g.torch.empty((w.num_query_tokens, w.num_q_heads, w.head_dim), dtype=g.torch.float32,
                         device=g.dev)
@@ -372,11 +375,12 @@ def bench_prefill(g: Gpu, steps: int, warmup: int, name: str = "C4"):
         "wall_s_timed_region": wall,
     }
     if name != "C4":
-        # same peak (bf16 and fp16 dense MFMA: 2.5 PFLOP/s); counters are
-        # taken for the bf16 batch only
+        # the peak of the MFMA the kernel runs: bf16 / fp16 dense 2.5 PFLOP/s
+        # (16-bit and one-byte caches), fp32 157.3 TFLOP/s (fp32 cache);
+        # counters are taken for the bf16 batch only
         res["roofline"] = {"bound": "mfma", "achieved": res["tflops_prefill_call"],
-                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": res["tflops_prefill_call"] / BF16_PEAK_TFLOPS, "traffic": None}
+                           "peak": peak, "unit": "TFLOP/s",
+                           "frac": res["tflops_prefill_call"] / peak, "traffic": None}
         return w, res, out
     res["roofline"] = {"bound": "mfma", "achieved": res["tflops_prefill_call"],
                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -547,7 +551,7 @@ def main():
                     help="seconds of oracle CPU work for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of workloads to run (C1..C5, C4i8, C4fp8, C4q32, M1, M2, R1, "
+                    help="comma list of workloads to run (C1..C5, C4i8, C4fp8, C4q32, C4f32, M1, M2, R1, "
                          "W1, F1); default all")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -556,7 +560,7 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     only = set(args.only.split(",")) if args.only else {"C1", "C2", "C3", "C4", "C5", "M1", "M2", "R1",
-                                                        "W1", "F1", "C4i8", "C4fp8", "C4q32"}
+                                                        "W1", "F1", "C4i8", "C4fp8", "C4q32", "C4f32"}
 
     g = Gpu()
     extras = {}
@@ -575,7 +579,7 @@ def main():
     if "C4" in only:
         _, rp, _ = bench_prefill(g, args.steps, args.warmup)
         extras["prefill_C4"] = rp
-    for name in ("C4i8", "C4fp8", "C4q32"):
+    for name in ("C4i8", "C4fp8", "C4q32", "C4f32"):
         if name in only:
             _, rp, _ = bench_prefill(g, args.steps, args.warmup, name)
             extras[f"prefill_{name}"] = rp

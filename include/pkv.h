@@ -311,13 +311,13 @@ size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_
  *   workspace      at least paged_attn_prefill_workspace_bytes(...) bytes.
  *   other arguments as for paged_attn_decode.
  *
- * Built for head_dim 64 and 128, page_size 16, kv_dtype PKV_BF16, PKV_F16,
- * PKV_I8 or PKV_FP8 (QK^T and PV on MFMA with fp32 accumulation; int8 and
- * FP8 codes are converted exactly to fp16, the query row is scaled by a
- * power of two before it is rounded to fp16, the K scales multiply the
- * scores and the V scales the probabilities); PKV_F32 returns
- * PKV_ERR_UNSUPPORTED.  k_scales and v_scales, when given, must be 16-byte
- * aligned (PKV_ERR_MISALIGNED).
+ * Built for head_dim 64 and 128, page_size 16 and every KV dtype (QK^T and
+ * PV on MFMA with fp32 accumulation: fp32 caches on the fp32 MFMA with P in
+ * fp32; 16-bit caches in their own type with P rounded to it; int8 and FP8
+ * codes converted exactly to fp16, the query row scaled by a power of two
+ * before it is rounded to fp16, the K scales on the scores and the V scales
+ * on the probabilities).  k_scales and v_scales, when given, must be
+ * 16-byte aligned (PKV_ERR_MISALIGNED).
  *
  * Non-finite cache values: a NaN or inf K or V value (int8/FP8: a NaN or
  * inf scale) at a position makes the rows that attend that position NaN or
@@ -360,9 +360,8 @@ size_t paged_attn_prefill_workspace_bytes(int batch, int num_q_heads, int num_kv
  *                  decode split partials; may be NULL when that is 0); its
  *                  contents on entry do not matter.
  *
- * Built for head_dim 64 and 128, page_size 16, kv_dtype PKV_BF16, PKV_F16,
- * PKV_I8 or PKV_FP8, decode keys spanning up to 262144 tokens
- * (PKV_ERR_UNSUPPORTED otherwise);
+ * Built for head_dim 64 and 128, page_size 16, every KV dtype, decode keys
+ * spanning up to 262144 tokens (PKV_ERR_UNSUPPORTED otherwise);
  * `window` as for paged_attn_prefill_chunk.  A one-token
  * chunk with context_lens[b] < 1 gets NaN, like any chunk longer than its
  * context.

@@ -51,11 +51,13 @@ template <int D, int KV>
 static void launch_mixed(const DecodeArgs& da, const PrefillArgs& pa, int n_prefill, int n_decode,
                          pkv_stream_t stream) {
   const dim3 grid(n_prefill + n_decode);
-  if (!prefill_q_split(KV, pa.q_dtype))
-    hipLaunchKernelGGL((mixed_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, da, pa,
-                       n_prefill);
+  bool split = false;
+  if constexpr (KV != PKV_F32) split = prefill_q_split(KV, pa.q_dtype);
+  if (split)
+    hipLaunchKernelGGL((mixed_kernel<D, KV, KV != PKV_F32>), grid, dim3(256), 0, (hipStream_t)stream,
+                       da, pa, n_prefill);
   else
-    hipLaunchKernelGGL((mixed_kernel<D, KV, true>), grid, dim3(256), 0, (hipStream_t)stream, da, pa,
+    hipLaunchKernelGGL((mixed_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, da, pa,
                        n_prefill);
   if (da.nsplits > 1)
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(da.hq, da.batch), dim3(64), 0,
@@ -69,7 +71,8 @@ static void dispatch_mixed(int kv, const DecodeArgs& da, const PrefillArgs& pa, 
     case PKV_BF16: launch_mixed<D, PKV_BF16>(da, pa, n_prefill, n_decode, stream); break;
     case PKV_F16: launch_mixed<D, PKV_F16>(da, pa, n_prefill, n_decode, stream); break;
     case PKV_I8: launch_mixed<D, PKV_I8>(da, pa, n_prefill, n_decode, stream); break;
-    default: launch_mixed<D, PKV_FP8>(da, pa, n_prefill, n_decode, stream); break;
+    case PKV_FP8: launch_mixed<D, PKV_FP8>(da, pa, n_prefill, n_decode, stream); break;
+    default: launch_mixed<D, PKV_F32>(da, pa, n_prefill, n_decode, stream); break;
   }
 }
 
@@ -125,7 +128,6 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim) ||
       !decode_span_supported(max_context_len, window))
     return PKV_ERR_UNSUPPORTED;
-  if (kv_dtype == PKV_F32) return PKV_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(block_tables) || !aligned16(context_lens) || !aligned16(cu_q_lens) ||
       (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)))

@@ -18,8 +18,9 @@ inline bool kv_dtype_ok(int dt) { return io_dtype_ok(dt) || kv_scaled(dt); }
 // Whether the prefill splits the query into head + remainder: a 16-bit
 // cache multiplies q in its own type (exact when q has that type), an
 // int8 / FP8 cache in fp16 (exact after a power-of-two row scaling for a
-// bf16 or fp16 q).
+// bf16 or fp16 q), an fp32 cache in fp32.
 inline bool prefill_q_split(int kv, int q_dtype) {
+  if (kv == PKV_F32) return false;   // fp32 MFMA: q exact in fp32
   return kv_scaled(kv) ? q_dtype == PKV_F32 : q_dtype != kv;
 }
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }

@@ -44,6 +44,8 @@
 // converted exactly to fp16 in registers, q scaled by a power of two and
 // rounded to fp16 (split for an fp32 q), the K scale on the score and the
 // V scale on the fp16 probability (prefill_body.h states the ranges).
+// fp32 caches: the 32x32x2 fp32 MFMA with P kept in fp32 (two stages of
+// 64 KB at head_dim 128: one workgroup per CU).
 #include "prefill_body.h"
 
 namespace pkv {
@@ -62,10 +64,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 template <int D, int KV>
 static void dispatch_prefill_q(const PrefillArgs& a, pkv_stream_t stream) {
   dim3 grid(a.batch, a.hkv, a.nrowblocks);
-  if (!prefill_q_split(KV, a.q_dtype))
-    hipLaunchKernelGGL((prefill_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, KV, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  if constexpr (KV != PKV_F32) {
+    if (prefill_q_split(KV, a.q_dtype)) {
+      hipLaunchKernelGGL((prefill_kernel<D, KV, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((prefill_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
 }
 
 template <int D>
@@ -74,7 +79,8 @@ static void dispatch_prefill(int kv, const PrefillArgs& a, pkv_stream_t stream) 
     case PKV_BF16: dispatch_prefill_q<D, PKV_BF16>(a, stream); break;
     case PKV_F16: dispatch_prefill_q<D, PKV_F16>(a, stream); break;
     case PKV_I8: dispatch_prefill_q<D, PKV_I8>(a, stream); break;
-    default: dispatch_prefill_q<D, PKV_FP8>(a, stream); break;
+    case PKV_FP8: dispatch_prefill_q<D, PKV_FP8>(a, stream); break;
+    default: dispatch_prefill_q<D, PKV_F32>(a, stream); break;
   }
 }
 
@@ -114,7 +120,6 @@ extern "C" int paged_attn_prefill_chunk(const void* q, int q_dtype, const void* 
   if (kv_scaled(kv_dtype) != (k_scales != nullptr) || kv_scaled(kv_dtype) != (v_scales != nullptr))
     return PKV_ERR_INVALID_ARG;
   if (page_size != PKV_PAGE_SIZE || !head_dim_built(head_dim)) return PKV_ERR_UNSUPPORTED;
-  if (kv_dtype == PKV_F32) return PKV_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(block_tables) || !aligned16(context_lens) || !aligned16(cu_q_lens) ||
       (k_scales && !aligned16(k_scales)) || (v_scales && !aligned16(v_scales)))

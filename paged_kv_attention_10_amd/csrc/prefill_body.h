@@ -62,7 +62,7 @@ struct PrefillArgs {
 // then (int8 / FP8) each page's 16 K scales and 16 V scales.
 template <int D, int KV>
 struct PrefillLds {
-  static constexpr int ES = kv_code8(KV) ? 1 : 2;    // bytes per cached element
+  static constexpr int ES = KV == PKV_F32 ? 4 : (kv_code8(KV) ? 1 : 2);   // bytes per element
   static constexpr int kRow = ES * D;                // bytes of one K row
   static constexpr int kPageBytes = kPage * kRow;    // one page of K (= one page of V^T)
   static constexpr int vOff = 4 * kPageBytes;        // V^T blocks after the 64 K rows
@@ -78,6 +78,14 @@ __device__ __forceinline__ int k_swizzle(int rr) {
   if constexpr (D == 128) return (rr ^ ((rr & 8) >> 1)) & 15;
   else return (rr ^ (rr >> 3)) & 7;
 }
+
+// fp32 K rows (D/4 chunks): chunk c in slot c ^ swz(rr) with the 16-slot
+// pattern above (rows are a multiple of 256 bytes, so the 16 rows a 16-lane
+// read touches land in 16 different slots).  fp32 V^T rows (16 keys, four
+// chunks): chunk c of row d in slot c ^ vswz(d), which puts the 16 rows of
+// a 16-lane read (64 bytes apart) in 16 different 16-byte bank slots.
+__device__ __forceinline__ int k_swizzle32(int rr) { return (rr ^ ((rr & 8) >> 1)) & 15; }
+__device__ __forceinline__ int v_swizzle32(int d) { return ((d >> 2) ^ (d >> 1)) & 3; }
 
 // The same for one-byte K rows (D bytes), which also depends on the parity
 // p of the page in the tile: a 16-lane fragment read touches rows 0-7 or
@@ -209,6 +217,8 @@ __device__ __forceinline__ f16x8 codes8_to_f16(u32x2 w) {
 template <int D, int KV, bool QSPLIT>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, int b, int g, int rb) {
   constexpr bool kI8 = kv_code8(KV);
+  constexpr bool kF32 = (KV == PKV_F32);
+  static_assert(!(kF32 && QSPLIT), "an fp32 cache takes the query in fp32");
   constexpr bool kBF16 = (KV == PKV_BF16);
   using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
   using L = PrefillLds<D, KV>;
@@ -269,8 +279,20 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   //      rounded to the MFMA type, split into head + remainder for an fp32
   //      or other-typed query, and the scores take c * 2^-e.
   H8 qhi[NSTEP], qlo[QSPLIT ? NSTEP : 1];
+  float qf[kF32 ? D / 2 : 1];   // fp32 cache: q[col][s + (D/2)*hh], exact in fp32
   float row_c = a.scale_log2;   // c * 2^-e for this row
-  if constexpr (!kI8 && !QSPLIT) {
+  if constexpr (kF32) {
+    with_io_dtype(a.q_dtype, [&](auto qdt) {
+      constexpr int QT = decltype(qdt)::value;
+      uint32_t bits[D / 16][8];
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) io_bits_vec<8, QT>(a.q, qrow + (D / 2) * hh + 8 * s, bits[s]);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[8 * s + i] = live ? io_value<QT>(bits[s][i]) * a.q_mul : 0.f;
+    });
+  } else if constexpr (!kI8 && !QSPLIT) {
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       const int d0 = 16 * s + 8 * hh;
@@ -349,8 +371,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     const int byte = 1024 * j + 16 * lane;          // position inside the page's K block
     const int rr = byte / L::kRow, slot = (byte % L::kRow) / 16;
     if constexpr (kI8) koff[j] = rr * L::kRow + ((slot ^ k_swizzle8<D>(wave & 1, rr)) * 16);
+    else if constexpr (kF32) koff[j] = rr * L::kRow + ((slot ^ k_swizzle32(rr & 15)) * 16);
     else koff[j] = rr * L::kRow + ((slot ^ k_swizzle<D>(rr)) * 16);
   }
+  // fp32 V^T rows are 64 bytes: the swizzle of row d = 16*j + lane/4 does
+  // not depend on j
+  const int voff = kF32 ? 64 * (lane >> 2) + (((lane & 3) ^ v_swizzle32(lane >> 2)) * 16) : 16 * lane;
   const char* sc_src = nullptr;
   if constexpr (kI8)
     sc_src = reinterpret_cast<const char*>(lane < 4 ? a.k_scales : a.v_scales) + 16 * (lane & 3);
@@ -369,7 +395,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
 #pragma unroll
       for (int j = 0; j < L::dmaPerPage; ++j) {
         dma16(kc + blk + koff[j], lk + 1024 * j);
-        dma16(vc + blk + 1024 * j + 16 * lane, lv + 1024 * j);
+        dma16(vc + blk + 1024 * j + voff, lv + 1024 * j);
       }
       if constexpr (kI8) {
         if (lane < 8)
@@ -401,9 +427,66 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     }
   };
 
-  if constexpr (!kI8) {
+  // ---- causal and window masks on the S^T registers: register r of half
+  //      hf holds key kb + base(hf) + roff(r), roff(r) a constant; keys past
+  //      the row's limit, or before its window, get -inf (only tiles that
+  //      cross one need the test).  The comparisons are against the row's
+  //      bound minus the half's base, so each register costs one compare
+  //      with a constant.
+  auto apply_masks = [&](f32x16 (&s)[2], int kb, auto base, auto roff) {
+    if (kb + 63 > lim_min) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int rel = limit - (kb + base(hf));   // largest allowed roff
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (roff(r) > rel) s[hf][r] = -INFINITY;
+      }
+    }
+    if (kb < win_max) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int rel = wlo - (kb + base(hf));     // smallest allowed roff
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (roff(r) < rel) s[hf][r] = -INFINITY;
+      }
+    }
+  };
+  // ---- lazy running max (log2 units): the accumulator is rescaled only when
+  //      a row's max grows by more than 2^8; returns the max to subtract
+  auto update_max = [&](float mt) {
+    const bool grow = mt > m_run + kLazyRescale;
+    if (__any(grow)) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
+      m_run = m_new;
+    }
+    return (m_run == -INFINITY) ? 0.f : m_run;
+  };
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float mt = s[0][0];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
+    return max_xor32(mt);
+  };
+  // keys at or past the context end, or in pages not read because they lie
+  // wholly before the window, may hold anything
+  auto edge_tile = [&](int kb) { return kb + 64 > ctx || kb < kPage * p_first; };
+  // the register layout of the 16-bit and fp32 paths: the A-operand row
+  // rho of S^T reads key 16*(rho/16) + 8*((rho/4)&1) + 4*((rho/8)&1) + rho%4,
+  // so register r of half hf holds key 32*hf + 16*(r/8) + 8*hh + r%8
+  const int krow = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
+  auto base16 = [&](int hf) { return 32 * hf + 8 * hh; };
+  auto roff16 = [](int r) { return 16 * (r >> 3) + (r & 7); };
+
+  if constexpr (!kI8 && !kF32) {
     // per-lane LDS offsets of the fragment reads
-    const int krow = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
     int kaddr[NSTEP];
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k)
@@ -443,9 +526,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
           for (int j = 0; j < 2; ++j)
             vfr[hf][db][j] = *reinterpret_cast<const u32x4*>(
                 st + vaddr + (2 * hf + j) * L::kPageBytes + db * 32 * 32);
-      // keys at or past the context end, or in pages not read because they
-      // lie wholly before the window, may hold anything: zero their V
-      if (kb + 64 > ctx || kb < kPage * p_first) {
+      // out-of-range keys may hold anything (NaN): zero their V
+      if (edge_tile(kb)) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -460,44 +542,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
             }
           }
       }
-      // ---- online softmax for query row `col`; register r of half hf holds
-      //      key kb + 32*hf + 16*(r/8) + 8*hh + r%8, masked when that exceeds
-      //      `limit`.  Raw scores are masked and maximised; the log2e-prescaled
-      //      scale (positive) is applied inside the exponent: p = 2^(s*c - m).
-      if (kb + 63 > lim_min) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int rel = limit - (kb + 32 * hf + 8 * hh);   // largest allowed 16*(r/8) + r%8
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (16 * (r >> 3) + (r & 7) > rel) s[hf][r] = -INFINITY;
-        }
-      }
-      if (kb < win_max) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int rel = wlo - (kb + 32 * hf + 8 * hh);     // smallest allowed 16*(r/8) + r%8
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (16 * (r >> 3) + (r & 7) < rel) s[hf][r] = -INFINITY;
-        }
-      }
-      float mt = s[0][0];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
-      mt = max_xor32(mt) * row_c;
-      const bool grow = mt > m_run + kLazyRescale;
-      if (__any(grow)) {
-        const float m_new = grow ? mt : m_run;
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_part *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      // ---- online softmax for query row `col` on raw scores; the
+      //      log2e-prescaled scale (positive) is applied inside the
+      //      exponent: p = 2^(s*c - m)
+      apply_masks(s, kb, base16, roff16);
+      const float m_use = update_max(tile_max(s) * row_c);
       float lsum = 0.f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -528,6 +577,69 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
             acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[hf][db][j]), p16[j], acc[db]);
       }
       l_part += lsum;
+    });
+  } else if constexpr (kF32) {
+    // fp32 cache, 32x32x2 fp32 MFMA: k-step s of the QK product pairs lane
+    // hh's d = (D/2)*hh + s, so a lane reads one contiguous half of its K
+    // row; PV k-step (page pg, e) pairs lane hh's key 16*pg + 8*hh + e, so a
+    // lane reads 8 contiguous keys of its V^T row d = 32*db + col per page
+    const int kbase = krow * L::kRow;
+    const int ksw = k_swizzle32(krow & 15);
+    const int vsw = v_swizzle32(col);          // the swizzle of row 32*db + col
+    const int vrow = L::vOff + col * 64;
+    run_tiles([&](const char* st, int kb) {
+      // ---- S^T = K * Q^T, the two halves' MFMA chains interleaved
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        f32x4 kf[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          kf[hf] = *reinterpret_cast<const f32x4*>(st + hf * 2 * L::kPageBytes + kbase +
+                                                   ((((D / 8) * hh + c) ^ ksw) * 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            s[hf] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[hf][e], qf[4 * c + e], s[hf], 0, 0, 0);
+      }
+      // ---- online softmax on raw scores, P kept in fp32
+      apply_masks(s, kb, base16, roff16);
+      const float m_use = update_max(tile_max(s) * row_c);
+      float lsum = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][r], row_c, -m_use));
+          lsum += s[hf][r];
+        }
+      l_part += lsum;
+      // ---- O^T += V^T * P^T; out-of-range keys may hold anything (NaN):
+      //      their V is zeroed
+      const bool edge = edge_tile(kb);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          const int key0 = kb + 32 * hf + 16 * pg + 8 * hh;
+          const int nv = key0 < kPage * p_first ? 0 : ctx - key0;   // in-range keys of the 8
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const char* vp = st + vrow + (2 * hf + pg) * L::kPageBytes + db * 32 * 64;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(vp + (((2 * hh) ^ vsw) * 16));
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(vp + (((2 * hh + 1) ^ vsw) * 16));
+            float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            if (edge) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (e >= nv) v[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[e], s[hf][8 * pg + e], acc[db], 0, 0, 0);
+          }
+        }
     });
   } else {
     // per-lane LDS offsets: the A-operand row col of S^T reads key
@@ -578,49 +690,16 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         }
       }
       // ---- scores in log2 units; register r of half hf holds key
-      //      kb + 32*hf + 16*hh + r, masked past `limit` and before `wlo`
+      //      kb + 32*hf + 16*hh + r
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[hf][r] *= ksc[hf][r >> 2][r & 3] * row_c;
-      if (kb + 63 > lim_min) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int rel = limit - (kb + 32 * hf + 16 * hh);
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (r > rel) s[hf][r] = -INFINITY;
-        }
-      }
-      if (kb < win_max) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int rel = wlo - (kb + 32 * hf + 16 * hh);
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (r < rel) s[hf][r] = -INFINITY;
-        }
-      }
-      float mt = s[0][0];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
-      mt = max_xor32(mt);
-      const bool grow = mt > m_run + kLazyRescale;
-      if (__any(grow)) {
-        const float m_new = grow ? mt : m_run;
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_part *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      // ---- V scales: keys at or past the context end, or in pages not read,
-      //      may hold anything (scales and, for FP8, NaN codes): their scale
-      //      is taken as 0 and their codes zeroed
-      const bool edge = kb + 64 > ctx || kb < kPage * p_first;
+      apply_masks(s, kb, [&](int hf) { return 32 * hf + 16 * hh; }, [](int r) { return r; });
+      const float m_use = update_max(tile_max(s));
+      // ---- V scales: out-of-range keys may hold anything (scales and, for
+      //      FP8, NaN codes): their scale is taken as 0 and their codes zeroed
+      const bool edge = edge_tile(kb);
       float vs[2][16];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {

@@ -122,7 +122,7 @@ def test_decode_rejects(lib, over, code):
 @pytest.mark.parametrize("over,code", [
     ({"q": None}, INVALID), ({"cu": None}, INVALID), ({"mql": 200}, INVALID),
     ({"T": -1}, INVALID), ({"hq": 3}, INVALID), ({"mcl": 200}, INVALID),
-    ({"kvd": 0}, UNSUPPORTED), ({"kvd": 3}, INVALID), ({"kvd": 4, "ks": FAKE}, INVALID),
+    ({"kvd": 0, "ks": FAKE, "vs": FAKE}, INVALID), ({"kvd": 3}, INVALID), ({"kvd": 4, "ks": FAKE}, INVALID),
     ({"kvd": 3, "ks": FAKE + 4, "vs": FAKE}, MISALIGNED), ({"kvd": 4, "ks": FAKE, "vs": FAKE + 8}, MISALIGNED),
     ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED), ({"cu": FAKE + 4}, MISALIGNED),
     ({"od": 3}, INVALID), ({"win": -5}, INVALID), ({"sc": float("nan")}, INVALID),
@@ -136,7 +136,7 @@ def test_prefill_rejects(lib, over, code):
 @pytest.mark.parametrize("over,code", [
     ({"cu": None}, INVALID), ({"bt": None}, INVALID), ({"mql": 200}, INVALID), ({"T": -1}, INVALID),
     ({"hq": 3}, INVALID), ({"mcl": 200}, INVALID), ({"B": 70000}, INVALID),
-    ({"kvd": 0}, UNSUPPORTED), ({"kvd": 4}, INVALID), ({"kvd": 3, "ks": FAKE, "vs": FAKE + 4}, MISALIGNED),
+    ({"kvd": 0, "vs": FAKE}, INVALID), ({"kvd": 4}, INVALID), ({"kvd": 3, "ks": FAKE, "vs": FAKE + 4}, MISALIGNED),
     ({"ps": 32}, UNSUPPORTED), ({"d": 80}, UNSUPPORTED),
     ({"mb": 20000, "mcl": 262160}, UNSUPPORTED),            # beyond the longest split context
     ({"cu": FAKE + 4}, MISALIGNED), ({"od": 3}, INVALID), ({"win": -1}, INVALID),

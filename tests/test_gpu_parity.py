@@ -269,7 +269,7 @@ def test_prefill_row_block_order(pkv, case):
     assert oracle.max_abs_err(got, ref) <= 1e-2
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f16", "i8", "fp8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "f16", "i8", "fp8"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (6, 2), (12, 2), (3, 1)])
 def test_prefill_small(pkv, kv, d, hq, hkv):
@@ -277,18 +277,29 @@ def test_prefill_small(pkv, kv, d, hq, hkv):
     ql = [16, 7, 17, 150, 1, 64]           # prefixes 0, 33, 0, 50, 32, 66
     w = small_prefill(ctx, ql, hq, hkv, d, kv, seed=hq + d)
     say(f"prefill small kv={kv} d={d} hq={hq} hkv={hkv}")
-    err = _prefill_check(pkv, w, oracle_cache(w), q_dtype=kv if kv in ("bf16", "f16") else "bf16")
-    assert err <= 1e-2, err
+    err = _prefill_check(pkv, w, oracle_cache(w), q_dtype=kv if kv in ("f32", "bf16", "f16") else "bf16")
+    assert err <= TOL[kv], err
 
 
 @pytest.mark.parametrize("kv,q_dtype", [("bf16", "f32"), ("bf16", "f16"), ("i8", "f32"), ("i8", "f16"),
-                                        ("fp8", "f32"), ("fp8", "f16")])
+                                        ("fp8", "f32"), ("fp8", "f16"), ("f32", "bf16"), ("f32", "f16")])
 @pytest.mark.parametrize("d", [64, 128])
 def test_prefill_q_other_dtype(pkv, kv, q_dtype, d):
     w = small_prefill([300, 90], [100, 90], 6, 2, d, kv, seed=8)
     say(f"prefill {kv} KV d={d} with q={q_dtype}")
     err = _prefill_check(pkv, w, oracle_cache(w), q_dtype=q_dtype)
-    assert err <= 1e-2, err
+    assert err <= TOL[kv], err
+
+
+def test_prefill_bench_batch_stored_fp32(pkv):
+    """The benchmarked prefill batch with an fp32 cache and fp32 query:
+    every row within the fp32 tolerance."""
+    w = make_workload("C4")
+    say("prefill C4 batch stored as f32")
+    cache = oracle_cache(w, "f32")
+    err = _prefill_check(pkv, w, cache, q_dtype="f32")
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL["f32"]
 
 
 def test_prefill_rows_match_decode(pkv):
