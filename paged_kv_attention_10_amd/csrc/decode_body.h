@@ -269,10 +269,6 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
                                                       int gy, int b) {
   constexpr bool kF32 = (KV == PKV_F32);
   constexpr bool kI8 = kv_code8(KV);   // int8 or FP8 codes, exact in fp16
-  // an FP8 code converts to 2^-8 times its value; the 2^8 goes on the K
-  // scales and, for V, into the final power-of-two rescale
-  constexpr float kCodeScale = (KV == PKV_FP8) ? 256.0f : 1.0f;
-  constexpr int kVShift = (KV == PKV_FP8) ? 8 : 0;
   constexpr bool kBF16 = (KV == PKV_BF16);
   using H8 = typename std::conditional<kBF16, bf16x8, f16x8>::type;
   constexpr int NSTEP = kF32 ? D / 4 : D / 32;    // QK MFMA k-steps
@@ -334,23 +330,48 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 
   float qf[kF32 ? NSTEP : 1];
   H8 qhi[kF32 ? 1 : NSTEP], qlo[kF32 ? 1 : NSTEP];
+  float head_c = a.scale_log2;   // scale * log2(e) * 2^-e for this lane's head
   if constexpr (kF32) {
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s)
       qf[s] = q_live ? io_value_sel(io_word_bits(qw[s >> 2], s & 3, a.q_dtype), a.q_dtype) : 0.f;
   } else {
+    float x[NSTEP][8];
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      float x[8];
+    for (int s = 0; s < NSTEP; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        x[e] = q_live ? io_value_sel(io_word_bits(qw[s], e, a.q_dtype), a.q_dtype) : 0.f;
+        x[s][e] = q_live ? io_value_sel(io_word_bits(qw[s], e, a.q_dtype), a.q_dtype) : 0.f;
+    if constexpr (!kBF16) {
+      // fp16 operands (fp16, int8 and FP8 caches): the head's query is scaled
+      // by the power of two 2^e that puts its largest magnitude in
+      // [2^14, 2^15), so that fp16's range holds it (a head of magnitude
+      // 1e6 would overflow otherwise); the scores take 2^-e.  The head's
+      // elements lie in lanes c, c+16, c+32, c+48.
+      uint32_t amk = 0;
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amk = max(amk, abs_key(x[s][e]));
+      amk = max(amk, (uint32_t)__shfl_xor((int)amk, 16));
+      amk = max(amk, (uint32_t)__shfl_xor((int)amk, 32));
+      const float am = __uint_as_float(amk);
+      // zero, inf or NaN heads keep e = 0
+      const int e2 = (am > 0.f && am <= 3.402823466e38f) ? 15 - __builtin_amdgcn_frexp_expf(am) : 0;
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[s][e] = __builtin_ldexpf(x[s][e], e2);
+      head_c = __builtin_ldexpf(a.scale_log2, -e2);
+    }
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
       if constexpr (kBF16) {
-        auto sp = split_bf16(x);
+        auto sp = split_bf16(x[s]);
         qhi[s] = sp.hi;
         qlo[s] = sp.lo;
       } else {
-        auto sp = split_f16(x);
+        auto sp = split_f16(x[s]);
         qhi[s] = sp.hi;
         qlo[s] = sp.lo;
       }
@@ -409,7 +430,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   for (int i = 0; i < NBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_part = 0.f;
-  // 8-bit caches: acc holds the output times 2^-(v_exp - 4 + kVShift), where
+  // 8-bit caches: acc holds the output times 2^-(v_exp - 4), where
   // v_exp is the binade of the largest V scale seen (see compute)
   int v_exp = -1000;
 
@@ -439,7 +460,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
           for (int h = 0; h < 2; ++h) {
             f16x8 kf;
             const u32x2 codes = u32x2{cur.k[u][s2i][2 * h], cur.k[u][s2i][2 * h + 1]};
-            if constexpr (KV == PKV_FP8) fp8x8_to_f16x8(codes, kf);
+            if constexpr (KV == PKV_FP8) fp8x8_to_f16x8_value(codes, kf);
             else i8x8_to_f16x8(codes, kf);
             sacc = mfma16x16x32(kf, qhi[2 * s2i + h], sacc);
             sacc = mfma16x16x32(kf, qlo[2 * s2i + h], sacc);
@@ -464,8 +485,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
     float sc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x = s2[e >> 2][e & 3] * a.scale_log2;
-      if constexpr (kI8) x *= cur.ks[e >> 2][e & 3] * kCodeScale;
+      float x = s2[e >> 2][e & 3] * head_c;
+      if constexpr (kI8) x *= cur.ks[e >> 2][e & 3];
       sc[e] = x;
     }
     if (partial) {
@@ -543,12 +564,17 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
         for (int e = 0; e < 8; ++e) pv[e] = p[e];
       }
       // V of tokens at or past the context end or before the window may
-      // hold anything: zero them
+      // hold anything (NaN; for FP8 the NaN codes): zero them.  int8 codes
+      // are always finite and take a zero scale above instead.
       u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+      u32x2 cmask = {~0u, ~0u};
       if (partial) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (tok0 + e >= ctx || tok0 + e < lo) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          if (tok0 + e >= ctx || tok0 + e < lo) {
+            vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            cmask[e >> 2] &= ~(0xffu << (8 * (e & 3)));
+          }
       }
       H8 phi, plo;
       if constexpr (kBF16) {
@@ -565,7 +591,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
         H8 vf;
         if constexpr (kI8) {
           f16x8 tmp;
-          if constexpr (KV == PKV_FP8) fp8x8_to_f16x8(cur.v8[blk], tmp);
+          if constexpr (KV == PKV_FP8) fp8x8_to_f16x8_value(partial ? cur.v8[blk] & cmask : cur.v8[blk], tmp);
           else i8x8_to_f16x8(cur.v8[blk], tmp);
           vf = tmp;
         } else {
@@ -629,7 +655,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
 #pragma unroll
     for (int i = 0; i < NBLK; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_ldexpf(acc[i][r], v_exp - 4 + kVShift);
+      for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_ldexpf(acc[i][r], v_exp - 4);
   }
 
   // ---- merge the four waves in LDS

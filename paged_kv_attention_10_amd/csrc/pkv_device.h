@@ -224,27 +224,6 @@ __device__ __forceinline__ void i8x8_to_f16x8(u32x2 w, f16x8& out) {
   }
 }
 
-// OCP FP8 E4M3 codes (4 per dword) -> fp16 holding exactly 2^-8 times the
-// code's value.  E4M3 has exponent bias 7 and fp16 bias 15, and E4M3's
-// subnormal binade (2^-6 * 0.m) lines up with fp16's (2^-14 * 0.m) under the
-// same shift, so the fp16 pattern sign<<15 | (code & 0x7f)<<7 reads as
-// value * 2^-8 for every finite code (the caller folds 2^8 into the scale).
-// v_perm places code c under bits 15..8 of its fp16 half; the magnitude
-// moves down one bit and the sign stays.
-__device__ __forceinline__ void fp8x8_to_f16x8(u32x2 w, f16x8& out) {
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t lo = __builtin_amdgcn_perm(0u, w[q], 0x010c000cu);   // codes 0, 1 -> bytes 1, 3
-    const uint32_t hi = __builtin_amdgcn_perm(0u, w[q], 0x030c020cu);   // codes 2, 3
-    const f16x2 a = __builtin_bit_cast(f16x2, (lo & 0x80008000u) | ((lo >> 1) & 0x3f803f80u));
-    const f16x2 b = __builtin_bit_cast(f16x2, (hi & 0x80008000u) | ((hi >> 1) & 0x3f803f80u));
-    out[4 * q + 0] = a[0];
-    out[4 * q + 1] = a[1];
-    out[4 * q + 2] = b[0];
-    out[4 * q + 3] = b[1];
-  }
-}
-
 // OCP FP8 E4M3 codes (4 per dword) -> fp16 holding the code's value:
 // gfx950's two-code convert to fp32 (v_cvt_pk_f32_fp8, which reads OCP
 // E4M3 on this chip: checked over all 256 codes, NaN codes giving NaN),

@@ -164,3 +164,27 @@ def test_decode_any_finite_scale(pkv, scale, kv):
     ref = oracle.ref_decode(w.q.astype(np.float64), cache, w.block_tables, w.context_lens, w.scale,
                             w.num_q_heads)
     assert oracle.max_abs_err(to_f64(out), ref) <= (2e-5 if kv == "f32" else 1e-2)
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8", "fp8", "bf16", "f32"])
+@pytest.mark.parametrize("q_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("k", [-60, 40])
+def test_decode_query_outside_fp16_range(pkv, kv, q_dtype, k):
+    """The query times 2^k with the scale times 2^-k (the same scores): the
+    fp16-operand decodes (fp16, int8 and FP8 caches) scale each head's query
+    by a power of two before the head + remainder split, so a query of 2^40
+    (past fp16's largest value) or 2^-60 (below its smallest) is held to
+    the usual tolerance."""
+    w = custom_workload(context_lens=[1, 40, 300, 1000, 2500], num_q_heads=8, num_kv_heads=2,
+                        head_dim=128, kv_dtype=kv, seed=33)
+    w.q = (w.q.astype(np.float64) * 2.0 ** k).astype(np.float32)
+    w.scale = np.float32(float(w.scale) * 2.0 ** -k)
+    say(f"decode kv={kv} q={q_dtype} query x 2^{k}")
+    cache = oracle_cache(w)
+    gc = poisoned_gpu_cache(cache, used_slot_mask(w))
+    q = torch.from_numpy(w.q).cuda().to(TORCH_DT[q_dtype])
+    assert torch.all(torch.isfinite(q))
+    out = run_decode(pkv, w, gc, q)
+    ref = oracle.ref_decode(q.double().cpu().numpy(), cache, w.block_tables, w.context_lens, w.scale,
+                            w.num_q_heads)
+    assert oracle.max_abs_err(to_f64(out), ref) <= (2e-5 if kv == "f32" else 1e-2)
