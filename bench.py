@@ -445,6 +445,51 @@ def bench_mixed(g: Gpu, name: str, steps: int, warmup: int):
     }
 
 
+def bench_ceiling(g: Gpu, sizes, steps: int, warmup: int):
+    """The practical streaming-read ceiling: libpkv_probe.so's read-only
+    kernel (hand-written HIP, outside the library, see csrc/probe.hip)
+    reads `nbytes` of a 1 GiB device buffer once, after the same 1 GiB
+    flush as every timed call, HIP events on the stream it runs on.  Three
+    grid sizes; the fastest is reported, labelled as a measured probe."""
+    import ctypes
+    torch = g.torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_attention_10_amd", "libpkv_probe.so"))
+    lib.pkv_probe_stream_read.restype = ctypes.c_int
+    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    buf = torch.zeros(1 << 30, dtype=torch.uint8, device=g.dev)
+    out = torch.zeros(1 << 14, dtype=torch.int32, device=g.dev)
+    stream = torch.cuda.current_stream()
+    res = []
+    for nbytes in sizes:
+        nbytes = min(int(nbytes) // 16 * 16, buf.numel())
+        best = None
+        for wg in (1024, 2048, 4096):
+            ms = []
+            for i in range(warmup + steps):
+                g.flush()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = lib.pkv_probe_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), wg,
+                                               ctypes.c_void_p(stream.cuda_stream))
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if rc != 0:
+                    raise RuntimeError(f"streaming-read probe failed ({rc})")
+                if i >= warmup:
+                    ms.append(e0.elapsed_time(e1))
+            st = stats(ms)
+            gbs = nbytes / (st["median"] * 1e-3) / 1e9
+            if best is None or gbs > best["gbs"]:
+                best = {"bytes": nbytes, "workgroups": wg, "call_ms": st, "gbs": gbs,
+                        "frac_of_peak": gbs / HBM_PEAK_GBS}
+        res.append(best)
+    return {"kind": "measured streaming-read probe (read-only HIP kernel outside the library, "
+                    "16-byte non-temporal loads, cold after the 1 GiB flush); median of the timed "
+                    "calls, fastest of 1024/2048/4096 workgroups",
+            "reads": res}
+
+
 def bench_rope(g: Gpu, steps: int, warmup: int):
     """R1: the fused append with RoPE (K rotated and stored, V stored, q
     rotated in place) against the plain append of the same K/V."""
@@ -595,6 +640,10 @@ def main():
         "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) q/K/V, scattered page tables)",
     }
+    ceiling = None
+    if "C2" in only:
+        ceiling = bench_ceiling(g, [head["effective_kv_bytes"], 1 << 30], args.steps, args.warmup)
+        extras["streaming_read_ceiling"] = ceiling
     if head is not None:
         line.update({
             "value": round(head["kv_gbs"], 2),
@@ -612,7 +661,12 @@ def main():
                          "traffic": profiled_traffic("decode_C2_counters.txt",
                                                      source_sha("decode.hip", "decode_body.h", "pkv_device.h", "pkv_host.h")),
                          "kernel": "paged_attn_decode_append call: decode_partition_kernel<128,bf16,fused> + decode_reduce_kernel<128>, events around both",
-                         "algorithmic_bytes_per_launch": head["effective_kv_bytes"]},
+                         "algorithmic_bytes_per_launch": head["effective_kv_bytes"],
+                         # the same bytes read by the plain streaming probe:
+                         # the practical ceiling, not the published peak
+                         "practical_ceiling_gbs": round(ceiling["reads"][0]["gbs"], 1) if ceiling else None,
+                         "frac_of_practical_ceiling": (round(head["decode_call_gbs"] / ceiling["reads"][0]["gbs"], 4)
+                                                       if ceiling else None)},
             "detail_C2": head,
         })
     line["extra"] = extras

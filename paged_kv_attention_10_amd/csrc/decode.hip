@@ -50,12 +50,11 @@
 
 namespace pkv {
 
-#ifndef PKV_DECODE_MIN_WAVES
-#define PKV_DECODE_MIN_WAVES 2
-#endif
+// Decode workgroups a CU holds at once (the register budget: 256 VGPRs).
+constexpr int kDecodeWorkgroupsPerCu = 2;
 
 template <int D, int KV, bool FUSE>
-__global__ __launch_bounds__(64 * kDecodeWaves, PKV_DECODE_MIN_WAVES) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves, kDecodeWorkgroupsPerCu) void decode_partition_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DecodeSmem<D>::total];
   decode_partition_body<D, KV, FUSE>(a, smem, blockIdx.x, blockIdx.y, blockIdx.z);
 }

@@ -33,7 +33,8 @@ constexpr int mixed_lds_bytes() {
 static_assert(64 * kDecodeWaves == 256, "both kinds of workgroup have 256 threads");
 
 template <int D, int KV, bool QSPLIT>
-__global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs da, PrefillArgs pa, int n_prefill) {
+__global__ __launch_bounds__(256, (prefill_workgroups_per_cu<D, KV>()))
+void mixed_kernel(DecodeArgs da, PrefillArgs pa, int n_prefill) {
   __shared__ __attribute__((aligned(1024))) char lds[mixed_lds_bytes<D, KV>()];
   const int id = blockIdx.x;
   if (id < n_prefill) {

@@ -58,10 +58,8 @@ struct DecodePlan {
 };
 
 constexpr int kDecodeTileTokens = 32;
-#ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4
-#endif
-constexpr int kDecodeWaves = PKV_DECODE_WAVES;
+// Waves of a decode workgroup (8 measured slower).
+constexpr int kDecodeWaves = 4;
 // A wave's page ids are held one per lane, so a wave takes at most 32 tiles.
 constexpr int kDecodeMaxTilesPerSplit = 32 * kDecodeWaves;
 // The merge kernel holds one split per lane.
@@ -72,10 +70,7 @@ constexpr long kDecodeMaxContext = (long)kDecodeMaxSplits * kDecodeMaxTilesPerSp
 // MI355X.  Fewer, longer splits measured faster than more, shorter ones:
 // every split pays a few dependent memory round trips before its first
 // tile streams and leaves a partial for the merge.
-#ifndef PKV_DECODE_TARGET_WORKGROUPS
-#define PKV_DECODE_TARGET_WORKGROUPS 256
-#endif
-constexpr long kDecodeTargetWorkgroups = PKV_DECODE_TARGET_WORKGROUPS;
+constexpr long kDecodeTargetWorkgroups = 256;
 
 // Tiles a sequence's keys span at most: its whole context, or with a
 // sliding window of `window` tokens the window, which may start anywhere in

@@ -51,7 +51,7 @@
 namespace pkv {
 
 template <int D, int KV, bool QSPLIT>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, (prefill_workgroups_per_cu<D, KV>())) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * PrefillLds<D, KV>::stage];
   int b = blockIdx.x, g = blockIdx.y;
   int rb = a.nrowblocks - 1 - (int)blockIdx.z;   // heavier (later) row blocks first

@@ -79,6 +79,13 @@ __device__ __forceinline__ int k_swizzle(int rr) {
   else return (rr ^ (rr >> 3)) & 7;
 }
 
+// Workgroups a CU can hold for this stage size (160 KB of LDS per CU): two
+// for the 16-bit and one-byte caches, one for fp32 at head_dim 128.
+template <int D, int KV>
+constexpr int prefill_workgroups_per_cu() {
+  return 2 * (2 * PrefillLds<D, KV>::stage) <= 160 * 1024 ? 2 : 1;
+}
+
 // fp32 K rows (D/4 chunks): chunk c in slot c ^ swz(rr) with the 16-slot
 // pattern above (rows are a multiple of 256 bytes, so the 16 rows a 16-lane
 // read touches land in 16 different slots).  fp32 V^T rows (16 keys, four
