@@ -197,10 +197,10 @@ def stats(xs):
 
 
 def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
-    """One step = the step's new tokens appended + the decode call.  With a
-    16- or 32-bit cache the step is one fused call (paged_attn_decode_append);
-    the same step as two calls (paged_kv_append, then paged_attn_decode) is
-    timed beside it.  int8/FP8 caches take the two calls."""
+    """One step = the step's new tokens appended + the decode call, as one
+    fused call (paged_attn_decode_append; int8 / FP8 caches quantise the
+    new rows in it); the same step as two calls (paged_kv_append, then
+    paged_attn_decode) is timed beside it."""
     from workloads import make_workload
     w = make_workload(name)
     log(f"[bench] {name}: building the pool on the GPU")
@@ -219,7 +219,7 @@ def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
     nws = g.pkv.paged_attn_decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads,
                                                   w.head_dim, w.max_context_len, window)
     ws = g.torch.zeros(max(nws, 16), dtype=g.torch.uint8, device=g.dev)
-    fused = w.kv_dtype in ("f32", "bf16", "f16")
+    fused = True
 
     def decode():
         g.pkv.paged_attn_decode(q, k, v, bt, cl, w.max_context_len, w.scale, out=out,
@@ -227,7 +227,8 @@ def bench_decode(g: Gpu, name: str, steps: int, warmup: int):
 
     def decode_step():
         g.pkv.paged_attn_decode_append(q, k_new, v_new, k, v, bt, cl, w.max_context_len, w.scale,
-                                       out=out, workspace=ws, window=window)
+                                       out=out, workspace=ws, window=window, k_scales=ks,
+                                       v_scales=vs)
 
     def two_calls(inner, e1=None, e2=None):
         g.pkv.paged_kv_append(k_new, v_new, slots_new, k, v, ks, vs)

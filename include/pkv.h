@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 #define PKV_PAGE_SIZE 16
 
 /* Element types.  PKV_BF16 is bfloat16 bits; PKV_I8 (int8 codes) and PKV_FP8
@@ -234,8 +234,13 @@ int paged_attn_decode(const void* q, int q_dtype,
  *   k_new, v_new   [batch][num_kv_heads][head_dim], dtype new_dtype
  *                  (F32/BF16/F16); read only.
  *   k_cache, v_cache  written at the new tokens' slots, read elsewhere.
- *   kv_dtype       PKV_F32, PKV_BF16 or PKV_F16 (int8 and FP8 quantise a
- *                  whole row and return PKV_ERR_UNSUPPORTED here).
+ *   k_scales, v_scales  required (non-NULL, 16-byte aligned) iff kv_dtype
+ *                  is PKV_I8 or PKV_FP8, NULL otherwise; written at the new
+ *                  tokens' slots (the vector's scale, exactly as
+ *                  paged_kv_append stores it), read elsewhere.
+ *   kv_dtype       any KV dtype.  int8 and FP8 quantise each new K and V
+ *                  vector with paged_kv_append's rule, so codes and scales
+ *                  are byte for byte those of paged_kv_append.
  *   other arguments as for paged_attn_decode; the workspace size is
  *                  paged_attn_decode_workspace_bytes(...).
  *
@@ -245,7 +250,8 @@ int paged_attn_decode(const void* q, int q_dtype,
  */
 int paged_attn_decode_append(const void* q, int q_dtype,
                              const void* k_new, const void* v_new, int new_dtype,
-                             void* k_cache, void* v_cache, int kv_dtype,
+                             void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                             int kv_dtype,
                              const int32_t* block_tables, int max_blocks_per_seq,
                              const int32_t* context_lens, int max_context_len,
                              int batch, int num_q_heads, int num_kv_heads, int head_dim,

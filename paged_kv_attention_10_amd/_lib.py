@@ -34,7 +34,7 @@ class PkvError(RuntimeError):
 _lib = None
 
 
-ABI_VERSION = 3   # PKV_ABI_VERSION of include/pkv.h this binding marshals for
+ABI_VERSION = 4   # PKV_ABI_VERSION of include/pkv.h this binding marshals for
 NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 
 
@@ -62,7 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       _c_float, _c_int, _vp, _c_int, _vp, _c_size, _vp]
     lib.paged_attn_decode_append.restype = _c_int
-    lib.paged_attn_decode_append.argtypes = [_vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp,
+    lib.paged_attn_decode_append.argtypes = [_vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp,
                                              _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_float, _c_int, _vp, _c_int, _vp,
                                              _c_size, _vp]
@@ -222,19 +222,22 @@ def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, m
 
 def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
                              max_context_len, scale, out=None, out_dtype=torch.float32,
-                             workspace=None, stream=None, window=0):
+                             workspace=None, stream=None, window=0, k_scales=None, v_scales=None):
     """One decode step: k_new/v_new [B, Hkv, d] go to position
-    context_lens[b] - 1, then q [B, Hq, d] attends -> out [B, Hq, d]."""
+    context_lens[b] - 1 (int8 / FP8 caches: quantised as paged_kv_append
+    does, scales written to k_scales / v_scales), then q [B, Hq, d]
+    attends -> out [B, Hq, d]."""
     B, hq, d = q.shape
     num_pages, hkv, page, _ = k_cache.shape
     if out is None:
         out = torch.empty((B, hq, d), dtype=out_dtype, device=q.device)
-    _dev(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, out)
+    _dev(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales)
     nbytes = paged_attn_decode_workspace_bytes(B, hq, hkv, d, max_context_len, window)
     workspace, wbytes = _workspace(nbytes, workspace, q.device)
     _check("paged_attn_decode_append", load_library().paged_attn_decode_append(
         _ptr(q), _code(q), _ptr(k_new), _ptr(v_new), _code(k_new), _ptr(k_cache), _ptr(v_cache),
-        _code(k_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+        _ptr(k_scales), _ptr(v_scales), _code(k_cache), _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(context_lens),
         int(max_context_len), B, hq, hkv, d, page, num_pages, float(scale), int(window),
         _ptr(out), _code(out), _ptr(workspace), wbytes, _stream(stream)))
     return out

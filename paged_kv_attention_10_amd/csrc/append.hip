@@ -230,23 +230,11 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
       for (int j = 0; j < 16; ++j) amk = max(amk, abs_key(x[j]));
 #pragma unroll
       for (int m = 1; m < NSEG; m <<= 1) amk = max(amk, (uint32_t)__shfl_xor((int)amk, m));
-      const float am = __uint_as_float(amk);
-      if (a.cache_dtype == PKV_I8) {
-        const float sc = am / 127.0f;
+      const bool i8 = a.cache_dtype == PKV_I8;
+      const float sc = code8_scale(__uint_as_float(amk), i8);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float code = 0.f;
-          if (sc > 0.f) code = fminf(fmaxf(rintf(x[j] / sc), -127.f), 127.f);
-          bits[j] = (uint32_t)(int)code & 0xffu;
-        }
-        if (s == 0) (is_v ? a.v_scales : a.k_scales)[head * kPage + off] = sc;
-      } else {
-        const float sc = am / 448.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          bits[j] = sc > 0.f ? f32_to_e4m3_bits(fminf(fmaxf(x[j] / sc, -448.f), 448.f)) : 0u;
-        if (s == 0) (is_v ? a.v_scales : a.k_scales)[head * kPage + off] = sc;
-      }
+      for (int j = 0; j < 16; ++j) bits[j] = code8(x[j], sc, i8);
+      if (s == 0) (is_v ? a.v_scales : a.k_scales)[head * kPage + off] = sc;
       if (!is_v) {
         int8_t* dst = static_cast<int8_t*>(a.k_cache) + (head * kPage + off) * D;
         *reinterpret_cast<u32x2*>(dst + c0) =
@@ -337,18 +325,11 @@ __device__ __forceinline__ void row_append(const AppendArgs& a, const void* src,
     for (int e = 0; e < PER; ++e) amk = max(amk, abs_key(x[e]));
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amk = max(amk, (uint32_t)__shfl_xor((int)amk, m));
-    const float am = __uint_as_float(amk);
     const bool i8 = a.cache_dtype == PKV_I8;
-    const float sc = am / (i8 ? 127.0f : 448.0f);
+    const float sc = code8_scale(__uint_as_float(amk), i8);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      uint32_t code = 0u;
-      if (sc > 0.f) {
-        if (i8) code = (uint32_t)(int)fminf(fmaxf(rintf(x[e] / sc), -127.f), 127.f) & 0xffu;
-        else code = f32_to_e4m3_bits(fminf(fmaxf(x[e] / sc, -448.f), 448.f));
-      }
-      static_cast<uint8_t*>(cache)[dst_index(lane * PER + e)] = (uint8_t)code;
-    }
+    for (int e = 0; e < PER; ++e)
+      static_cast<uint8_t*>(cache)[dst_index(lane * PER + e)] = (uint8_t)code8(x[e], sc, i8);
     if (lane == 0) scales[head * kPage + off] = sc;
     return;
   }

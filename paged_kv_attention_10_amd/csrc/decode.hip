@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void append_step_kernel(DecodeArgs a) {
   if (bad || ctx < 1) return;
   const int page = a.block_tables[(long)b * a.max_blocks + ((ctx - 1) >> 4)];
   if ((unsigned)page >= (unsigned)a.num_pages) return;
-  __shared__ __attribute__((aligned(16))) char stash[4][2 * D * 4];
+  __shared__ __attribute__((aligned(16))) char stash[4][kStashBytes<D>];
   stash_new_token<D, KV>(stash[threadIdx.x >> 6], nr, a, g, page, (ctx - 1) & 15, true, lane);
 }
 
@@ -91,17 +91,15 @@ template <int D, int KV>
 static void launch_decode(const DecodeArgs& a, pkv_stream_t stream) {
   dim3 grid(a.nsplits, a.hkv * a.head_tiles, a.batch);
   const bool fuse = a.k_new && (long)grid.x * grid.y * grid.z <= kFuseMaxWorkgroups;
-  if constexpr (!kv_code8(KV)) {
-    if (a.k_new && !fuse)
-      hipLaunchKernelGGL((append_step_kernel<D, KV>), dim3((unsigned)(((long)a.batch * a.hkv + 3) / 4)),
-                         dim3(256), 0, (hipStream_t)stream, a);
-  }
-  if (kv_code8(KV) || !fuse)
+  if (a.k_new && !fuse)
+    hipLaunchKernelGGL((append_step_kernel<D, KV>), dim3((unsigned)(((long)a.batch * a.hkv + 3) / 4)),
+                       dim3(256), 0, (hipStream_t)stream, a);
+  if (!fuse)
     hipLaunchKernelGGL((decode_partition_kernel<D, KV, false>), grid, dim3(64 * kDecodeWaves), 0,
                        (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<D, KV, !kv_code8(KV)>), grid, dim3(64 * kDecodeWaves),
-                       0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<D, KV, true>), grid, dim3(64 * kDecodeWaves), 0,
+                       (hipStream_t)stream, a);
   if (a.nsplits > 1)
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.hq, a.batch), dim3(64), 0,
                        (hipStream_t)stream, a);
@@ -199,6 +197,8 @@ static int decode_call(const void* q, int q_dtype, const void* k_cache, const vo
   a.new_dtype = new_dtype;
   a.k_store = const_cast<void*>(k_cache);
   a.v_store = const_cast<void*>(v_cache);
+  a.ks_store = const_cast<float*>(k_scales);
+  a.vs_store = const_cast<float*>(v_scales);
 
   clear_launch_error();
   if (head_dim == 64) dispatch_kv<64>(kv_dtype, a, stream);
@@ -222,7 +222,8 @@ extern "C" int paged_attn_decode(const void* q, int q_dtype, const void* k_cache
 
 extern "C" int paged_attn_decode_append(const void* q, int q_dtype, const void* k_new,
                                         const void* v_new, int new_dtype, void* k_cache,
-                                        void* v_cache, int kv_dtype, const int32_t* block_tables,
+                                        void* v_cache, float* k_scales, float* v_scales,
+                                        int kv_dtype, const int32_t* block_tables,
                                         int max_blocks_per_seq, const int32_t* context_lens,
                                         int max_context_len, int batch, int num_q_heads,
                                         int num_kv_heads, int head_dim, int page_size,
@@ -231,8 +232,7 @@ extern "C" int paged_attn_decode_append(const void* q, int q_dtype, const void* 
                                         pkv_stream_t stream) {
   if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
   if (!io_dtype_ok(new_dtype) || !kv_dtype_ok(kv_dtype)) return PKV_ERR_INVALID_ARG;
-  if (kv_scaled(kv_dtype)) return PKV_ERR_UNSUPPORTED;
-  return decode_call(q, q_dtype, k_cache, v_cache, nullptr, nullptr, kv_dtype, block_tables,
+  return decode_call(q, q_dtype, k_cache, v_cache, k_scales, v_scales, kv_dtype, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                      num_kv_heads, head_dim, page_size, num_pages, scale, window, out, out_dtype,
                      workspace, workspace_bytes, k_new, v_new, new_dtype, stream);

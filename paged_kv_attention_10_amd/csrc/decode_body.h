@@ -32,13 +32,15 @@ struct DecodeArgs {
   float scale_log2;
   // Fused decode step (null k_new: none): each sequence's new K/V row
   // [batch][hkv][D] in new_dtype is stored at position ctx - 1 (through the
-  // block table) and attended from registers; k_store/v_store are the
-  // writable cache pointers.
+  // block table) and attended from registers; k_store/v_store (and for
+  // int8 / FP8 ks_store/vs_store) are the writable cache pointers.
   const void* k_new;
   const void* v_new;
   int new_dtype;
   void* k_store;
   void* v_store;
+  float* ks_store;
+  float* vs_store;
 };
 
 // First position a query at position ctx - 1 attends: ctx - window with a
@@ -134,8 +136,9 @@ __device__ __forceinline__ int tile_row_of_lane(int r) {
   return (r < 8 ? 0 : 16) + 8 * ((r >> 2) & 1) + (r & 3);
 }
 
-// The new token's values this lane converts: K chunk `lane` (16 bytes of
-// storage, 16/ES elements) for lanes below D*ES/16, and V elements
+// The new token's values this lane converts: for 16- and 32-bit caches K
+// chunk `lane` (16 bytes of storage, 16/ES elements) for lanes below
+// D*ES/16, for one-byte caches K elements d = lane + 64h; V elements
 // d = lane + 64h.  Loaded as fp32 (exact for every input dtype; an fp32
 // value's bits are kept).
 template <int D>
@@ -144,12 +147,34 @@ struct NewRaw {
   float v[D / 64];
 };
 
+// Bytes of the per-wave stash of the new token: K and V as stored plus,
+// for one-byte caches, the two scales.
+template <int D>
+constexpr int kStashBytes = 2 * D * 4;
+
 template <int D, int KV>
 __device__ __forceinline__ void load_new_token(NewRaw<D>& nr, const DecodeArgs& a, int b, int g,
                                                int lane) {
+  const long nrow = ((long)b * a.hkv + g) * D;
+  if constexpr (kv_code8(KV)) {
+    with_io_dtype(a.new_dtype, [&](auto ndt) {
+      constexpr int NT = decltype(ndt)::value;
+      uint32_t kb[D / 64], vb[D / 64];
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h) {
+        kb[h] = io_bits<NT>(a.k_new, nrow + lane + 64 * h);
+        vb[h] = io_bits<NT>(a.v_new, nrow + lane + 64 * h);
+      }
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h) {
+        nr.k[h] = io_value<NT>(kb[h]);
+        nr.v[h] = io_value<NT>(vb[h]);
+      }
+    });
+    return;
+  }
   constexpr int ES = (KV == PKV_F32) ? 4 : 2;
   constexpr int KE = 16 / ES;                       // K elements per chunk
-  const long nrow = ((long)b * a.hkv + g) * D;
   const int kc = lane < D * ES / 16 ? lane : 0;     // lanes past the chunks reload chunk 0
   with_io_dtype(a.new_dtype, [&](auto ndt) {
     constexpr int NT = decltype(ndt)::value;
@@ -164,13 +189,61 @@ __device__ __forceinline__ void load_new_token(NewRaw<D>& nr, const DecodeArgs& 
   });
 }
 
+// One-byte caches: quantises the new K and V vectors as the append does
+// (code8_scale / code8 on the wave's absmax), writes the codes (K at stash
+// byte d, V at D + d) and the two scales (bytes 2D and 2D + 4) to the
+// stash and, with `store`, the codes and scales to the cache slot.
+template <int D, int KV>
+__device__ __forceinline__ void stash_new_token8(char* stash, const NewRaw<D>& nr,
+                                                 const DecodeArgs& a, int g, long page, int off,
+                                                 bool store, int lane) {
+  constexpr bool kI8 = (KV == PKV_I8);
+  uint32_t kam = 0u, vam = 0u;
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    kam = max(kam, abs_key(nr.k[h]));
+    vam = max(vam, abs_key(nr.v[h]));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    kam = max(kam, (uint32_t)__shfl_xor((int)kam, m));
+    vam = max(vam, (uint32_t)__shfl_xor((int)vam, m));
+  }
+  const float ksc = code8_scale(__uint_as_float(kam), kI8);
+  const float vsc = code8_scale(__uint_as_float(vam), kI8);
+  const long head = page * a.hkv + g;
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    const int d = lane + 64 * h;
+    const uint8_t kc = (uint8_t)code8(nr.k[h], ksc, kI8);
+    const uint8_t vc = (uint8_t)code8(nr.v[h], vsc, kI8);
+    reinterpret_cast<uint8_t*>(stash)[d] = kc;
+    reinterpret_cast<uint8_t*>(stash)[D + d] = vc;
+    if (store) {
+      static_cast<uint8_t*>(a.k_store)[(head * kPage + off) * D + d] = kc;
+      static_cast<uint8_t*>(a.v_store)[(head * D + d) * kPage + off] = vc;
+    }
+  }
+  if (lane == 0) {
+    reinterpret_cast<float*>(stash + 2 * D)[0] = ksc;
+    reinterpret_cast<float*>(stash + 2 * D)[1] = vsc;
+    if (store) {
+      a.ks_store[head * kPage + off] = ksc;
+      a.vs_store[head * kPage + off] = vsc;
+    }
+  }
+}
+
 // Converts the loaded new token into the wave's stash and, with `store`,
 // writes it to the cache slot (page, off), rounding as the append rounds.
 template <int D, int KV>
 __device__ __forceinline__ void stash_new_token(char* stash, const NewRaw<D>& nr,
                                                 const DecodeArgs& a, int g, long page, int off,
                                                 bool store, int lane) {
-  static_assert(!kv_code8(KV), "the fused step stores 16- and 32-bit caches");
+  if constexpr (kv_code8(KV)) {
+    stash_new_token8<D, KV>(stash, nr, a, g, page, off, store, lane);
+    return;
+  }
   constexpr int ES = (KV == PKV_F32) ? 4 : 2;
   auto conv = [](float x) -> uint32_t {
     if constexpr (KV == PKV_F32) return __float_as_uint(x);
@@ -210,14 +283,14 @@ __device__ __forceinline__ void stash_new_token(char* stash, const NewRaw<D>& nr
 template <int D, int KV>
 __device__ __forceinline__ void patch_new_token(DecodeTile<D, KV>& t, const char* stash, int tau,
                                                 int lane) {
-  constexpr int ES = (KV == PKV_F32) ? 4 : 2;
+  constexpr int ES = (KV == PKV_F32) ? 4 : (kv_code8(KV) ? 1 : 2);
   constexpr int KL = DecodeTile<D, KV>::KL;
   const int r = lane & 15, kg = lane >> 4;
   const int base = tile_row_of_lane(r);
   const bool k0 = tau == base, k1 = tau == base + 4;
 #pragma unroll
   for (int s = 0; s < KL; ++s) {
-    const int d0 = (KV == PKV_F32) ? 16 * s + 4 * kg : 32 * s + 8 * kg;
+    const int d0 = (KV == PKV_F32) ? 16 * s + 4 * kg : (kv_code8(KV) ? 64 * s + 16 * kg : 32 * s + 8 * kg);
     const u32x4 w = *reinterpret_cast<const u32x4*>(stash + d0 * ES);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -227,6 +300,28 @@ __device__ __forceinline__ void patch_new_token(DecodeTile<D, KV>& t, const char
   }
   const bool vl = kg == (tau >> 3);
   const int e = tau & 7;
+  if constexpr (kv_code8(KV)) {
+    // V code byte e of the lane's 8 tokens, and the two scales of token e
+    const float ksc = reinterpret_cast<const float*>(stash + 2 * D)[0];
+    const float vsc = reinterpret_cast<const float*>(stash + 2 * D)[1];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      t.ks[q >> 2][q & 3] = (vl && q == e) ? ksc : t.ks[q >> 2][q & 3];
+      t.vs[q >> 2][q & 3] = (vl && q == e) ? vsc : t.vs[q >> 2][q & 3];
+    }
+#pragma unroll
+    for (int blk = 0; blk < D / 16; ++blk) {
+      const uint32_t nv = reinterpret_cast<const uint8_t*>(stash + D)[16 * blk + r];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t w = t.v8[blk][q];
+        const int sh = 8 * (e & 3);
+        const uint32_t pw = (w & ~(0xffu << sh)) | (nv << sh);
+        t.v8[blk][q] = (vl && q == (e >> 2)) ? pw : w;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int blk = 0; blk < D / 16; ++blk) {
     const int d = 16 * blk + r;
@@ -406,8 +501,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   //      the new token from k_new / v_new (loaded now, ahead of its tiles),
   //      stores it to the cache (the first head tile only) and patches it
   //      into the tile it streams
-  constexpr bool kFusable = FUSE && !kv_code8(KV);
-  char* const stash = smem + SM::o + wave * 2 * D * ((KV == PKV_F32) ? 4 : 2);
+  constexpr bool kFusable = FUSE;
+  char* const stash = smem + SM::o + wave * kStashBytes<D>;
   int t_new = -1, tau_new = 0, page_new = 0;
   bool store_new = false;
   NewRaw<D> nr;
@@ -609,45 +704,54 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   //      holds no conditional loads or stores: the wait before a tile
   //      computes then covers only that tile's loads, not the next tile's
   //      issued just before (a load skipped on some path makes the wait
-  //      count for every path the worst one).  Tiles go in pairs; the one
-  //      load past the run's end reloads its last tile (from L2) and is
-  //      never computed.
+  //      count for every path the worst one).  The wave's last tile (or
+  //      last two) run after the loop: the fused step's new token, at
+  //      position ctx - 1, always lies in the wave's last tile (the tile
+  //      holding ctx - 1 is the context's last, and a wave's tiles are a
+  //      contiguous run), so it is patched in there, outside the loop (a
+  //      conditional patch inside it made the compiler copy and drain the
+  //      ring on every iteration).
   DecodeTile<D, KV> ring[R];
+  if constexpr (kFusable) {
+    // the new token's loads went out ahead of the first tile's, so this
+    // waits only for them
+    if (t_new >= 0) stash_new_token<D, KV>(stash, nr, a, g, page_new, tau_new & 15, store_new, lane);
+  }
   if constexpr (R == 1) {
-    for (int i = 0; i < ntw; ++i) {
+    int i = 0;
+    for (; i + 1 < ntw; ++i) {
+      issue(ring[0], i);
+      compute(ring[0], i);
+    }
+    if (i < ntw) {
       issue(ring[0], i);
       if constexpr (kFusable) {
-        if (i == 0 && t_new >= 0)
-          stash_new_token<D, KV>(stash, nr, a, g, page_new, tau_new & 15, store_new, lane);
-        if (i == t_new) patch_new_token<D, KV>(ring[0], stash, tau_new, lane);
+        if (t_new == i) patch_new_token<D, KV>(ring[0], stash, tau_new, lane);
       }
       compute(ring[0], i);
     }
   } else {
     static_assert(R == 2, "a ring of one or two tiles");
     if (ntw > 0) issue(ring[0], 0);
-    if constexpr (kFusable) {
-      // the new token's loads went out ahead of the first tile's, so this
-      // waits only for them
-      if (t_new >= 0) stash_new_token<D, KV>(stash, nr, a, g, page_new, tau_new & 15, store_new, lane);
-    }
-    for (int i = 0; i + 1 < ntw; i += 2) {
+    int i = 0;
+    for (; i + 2 < ntw; i += 2) {
       issue(ring[1], i + 1);
-      if constexpr (kFusable) {
-        if (i == t_new) patch_new_token<D, KV>(ring[0], stash, tau_new, lane);
-      }
       compute(ring[0], i);
-      issue(ring[0], min(i + 2, ntw - 1));
-      if constexpr (kFusable) {
-        if (i + 1 == t_new) patch_new_token<D, KV>(ring[1], stash, tau_new, lane);
-      }
+      issue(ring[0], i + 2);
       compute(ring[1], i + 1);
     }
-    if (ntw & 1) {
+    if (i + 1 < ntw) {          // two tiles left, i in ring[0]
+      issue(ring[1], i + 1);
+      compute(ring[0], i);
       if constexpr (kFusable) {
-        if (ntw - 1 == t_new) patch_new_token<D, KV>(ring[0], stash, tau_new, lane);
+        if (t_new == i + 1) patch_new_token<D, KV>(ring[1], stash, tau_new, lane);
       }
-      compute(ring[0], ntw - 1);
+      compute(ring[1], i + 1);
+    } else if (i < ntw) {       // one tile left, in ring[0]
+      if constexpr (kFusable) {
+        if (t_new == i) patch_new_token<D, KV>(ring[0], stash, tau_new, lane);
+      }
+      compute(ring[0], i);
     }
   }
   const float l_run = wave_sum_xor_16_32(l_part);

@@ -170,6 +170,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   da.k_new = da.v_new = nullptr;
   da.new_dtype = PKV_F32;
   da.k_store = da.v_store = nullptr;
+  da.ks_store = da.vs_store = nullptr;
 
   PrefillArgs pa;
   pa.q = q;

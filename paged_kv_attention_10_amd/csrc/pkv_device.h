@@ -258,6 +258,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_bits(float r) {
   return ((u >> 24) & 0x80u) | (uint32_t)(((e + 7) << 3) + (int)q - 8);
 }
 
+// The append's quantisation of one (token, KV head) vector, shared by every
+// kernel that stores one-byte codes so that they store the same bytes.
+// `am` is the vector's absmax taken as a sort key with abs_key (a NaN
+// element makes it NaN); the scale is am/127 (int8) or am/448 (FP8) in IEEE
+// fp32 division, and each code is clamp(rint(x/scale), -127, 127) (int8)
+// or the E4M3 value nearest to clamp(x/scale, -448, 448) (FP8); a scale
+// that is not positive (all-zero or NaN vector) gives codes 0.
+__device__ __forceinline__ float code8_scale(float am, bool i8) { return am / (i8 ? 127.0f : 448.0f); }
+
+__device__ __forceinline__ uint32_t code8(float x, float sc, bool i8) {
+  if (!(sc > 0.f)) return 0u;
+  if (i8) return (uint32_t)(int)fminf(fmaxf(rintf(x / sc), -127.f), 127.f) & 0xffu;
+  return f32_to_e4m3_bits(fminf(fmaxf(x / sc, -448.f), 448.f));
+}
+
 // Cross-lane exchanges with the gfx950 lane-swap instructions (VALU, no LDS
 // round trip).  v_permlane32_swap exchanges the upper 32 lanes of one
 // operand with the lower 32 of the other; given x in both, the two results

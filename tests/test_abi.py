@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 3 == _lib.ABI_VERSION
+    assert lib.pkv_abi_version() == 4 == _lib.ABI_VERSION
     for code in range(7):
         assert lib.pkv_status_string(code).decode().startswith("PKV_")
     assert lib.pkv_status_string(99).decode() == "PKV_ERR_UNKNOWN"
@@ -206,9 +206,9 @@ def test_append_rope_zero_tokens_is_noop(lib):
 
 
 def _decode_append(lib, **over):
-    a = dict(q=FAKE, qd=0, kn=FAKE, vn=FAKE, nd=0, k=FAKE, v=FAKE, kvd=1, bt=FAKE, mb=8, cl=FAKE,
-             mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125, win=0, out=FAKE, od=0,
-             ws=FAKE, wsb=1 << 20, st=None)
+    a = dict(q=FAKE, qd=0, kn=FAKE, vn=FAKE, nd=0, k=FAKE, v=FAKE, ks=None, vs=None, kvd=1, bt=FAKE,
+             mb=8, cl=FAKE, mcl=100, B=2, hq=4, hkv=2, d=64, ps=16, np_=32, sc=0.125, win=0,
+             out=FAKE, od=0, ws=FAKE, wsb=1 << 20, st=None)
     a.update(over)
     return lib.paged_attn_decode_append(*a.values())
 
@@ -216,7 +216,9 @@ def _decode_append(lib, **over):
 @pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run only without a GPU")
 @pytest.mark.parametrize("over,code", [
     ({"kn": None}, INVALID), ({"vn": None}, INVALID), ({"nd": 3}, INVALID), ({"q": None}, INVALID),
-    ({"kvd": 3}, UNSUPPORTED), ({"kvd": 4}, UNSUPPORTED), ({"kvd": 5}, INVALID),
+    ({"kvd": 3}, INVALID), ({"kvd": 4, "ks": FAKE}, INVALID), ({"kvd": 5}, INVALID),
+    ({"ks": FAKE, "vs": FAKE}, INVALID),                    # scales with a 16-bit cache
+    ({"kvd": 3, "ks": FAKE + 4, "vs": FAKE}, MISALIGNED),
     ({"hq": 5}, INVALID), ({"win": -1}, INVALID), ({"d": 96}, UNSUPPORTED),
     ({"sc": float("nan")}, INVALID),
     ({"kn": FAKE + 4}, MISALIGNED), ({"vn": FAKE + 2}, MISALIGNED),

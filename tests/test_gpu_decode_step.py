@@ -51,13 +51,14 @@ def _fused(pkv, w, gc, q, kn, vn, window=0, block_tables=None):
     bt = w.block_tables if block_tables is None else block_tables
     out = pkv.paged_attn_decode_append(q, kn, vn, gc["k"], gc["v"], np_to_gpu(bt),
                                        np_to_gpu(w.context_lens), w.max_context_len, w.scale,
-                                       window=window)
+                                       window=window, k_scales=gc["ks"], v_scales=gc["vs"])
     torch.cuda.synchronize()
     return out
 
 
 @pytest.mark.parametrize("kv,new_dtype", [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16"),
-                                          ("f32", "f32"), ("f32", "bf16")])
+                                          ("f32", "f32"), ("f32", "bf16"), ("i8", "f32"),
+                                          ("i8", "bf16"), ("fp8", "f32"), ("fp8", "f16")])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("hq,hkv", [(12, 2), (8, 8), (40, 2)])
 def test_decode_step_matches_oracle(pkv, kv, new_dtype, d, hq, hkv):
@@ -75,9 +76,30 @@ def test_decode_step_matches_oracle(pkv, kv, new_dtype, d, hq, hkv):
     gk, gv = gpu_to_np_bits(gc["k"]), gpu_to_np_bits(gc["v"])
     assert np.array_equal(np.where(mk, gk, 0).view(np.uint8), np.where(mk, cache.k, 0).view(np.uint8))
     assert np.array_equal(np.where(mv, gv, 0).view(np.uint8), np.where(mv, cache.v, 0).view(np.uint8))
+    if kv in ("i8", "fp8"):
+        for g_s, h_s in ((gc["ks"], cache.k_scales), (gc["vs"], cache.v_scales)):
+            got = g_s.cpu().numpy()
+            ms = used[:, None, :]
+            assert np.array_equal(np.where(ms, got, 0).view(np.uint32), np.where(ms, h_s, 0).view(np.uint32))
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def _append_then_decode(pkv, w, gc, q, kn, vn, last, window=0):
+    pkv.paged_kv_append(kn, vn, torch.from_numpy(w.slot_mapping[last]).cuda(), gc["k"], gc["v"],
+                        gc["ks"], gc["vs"])
+    out = pkv.paged_attn_decode(q, gc["k"], gc["v"], np_to_gpu(w.block_tables),
+                                np_to_gpu(w.context_lens), w.max_context_len, w.scale, window=window,
+                                k_scales=gc["ks"], v_scales=gc["vs"])
+    torch.cuda.synchronize()
+    return out
+
+
+def _same_cache(gc, gc2):
+    for key in ("k", "v", "ks", "vs"):
+        if gc[key] is not None:
+            assert torch.equal(gc[key].view(torch.uint8), gc2[key].view(torch.uint8)), key
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32", "i8", "fp8"])
 @pytest.mark.parametrize("window", [0, 40])
 def test_decode_step_equals_append_then_decode(pkv, kv, window):
     """The fused step and the two calls give the same cache and the same
@@ -89,13 +111,9 @@ def test_decode_step_equals_append_then_decode(pkv, kv, window):
     gc2 = {k: (None if t is None else t.clone()) for k, t in gc.items()}
     q = q_tensor(w, "f32")
     fused = _fused(pkv, w, gc, q, kn, vn, window=window)
-    pkv.paged_kv_append(kn, vn, torch.from_numpy(w.slot_mapping[last]).cuda(), gc2["k"], gc2["v"])
-    two = pkv.paged_attn_decode(q, gc2["k"], gc2["v"], np_to_gpu(w.block_tables),
-                                np_to_gpu(w.context_lens), w.max_context_len, w.scale, window=window)
-    torch.cuda.synchronize()
+    two = _append_then_decode(pkv, w, gc2, q, kn, vn, last, window=window)
     assert torch.equal(fused, two)
-    assert torch.equal(gc["k"].view(torch.uint8), gc2["k"].view(torch.uint8))
-    assert torch.equal(gc["v"].view(torch.uint8), gc2["v"].view(torch.uint8))
+    _same_cache(gc, gc2)
 
 
 def test_decode_step_empty_and_bad(pkv):
@@ -154,3 +172,64 @@ def test_decode_step_many_workgroups(pkv):
     oracle.ref_append(cache, w.k[last], w.v[last], w.slot_mapping[last])
     ref = oracle.ref_decode(q_exact_values(q), cache, w.block_tables, w.context_lens, w.scale, 12)
     assert oracle.max_abs_err(to_f64(out), ref) <= 1e-2
+
+
+@pytest.mark.parametrize("name,kv", [("C5", "i8"), ("F1", "fp8")])
+def test_decode_step_full_size_one_byte_caches(pkv, name, kv):
+    """The benchmarked int8 and FP8 steps in one launch: the new rows are
+    quantised in the partition kernel (codes and scales byte for byte those
+    of paged_kv_append, output bit for bit that of append + decode) and the
+    output is within tolerance of the oracle."""
+    from workloads import make_workload
+    say(f"decode step full size ({name}, {kv})")
+    w = make_workload(name)
+    cache, gc, kn, vn, last = _setup(w, kv, "f32")
+    gc2 = {k: (None if t is None else t.clone()) for k, t in gc.items()}
+    q = q_tensor(w, "f32")
+    out = _fused(pkv, w, gc, q, kn, vn)
+    two = _append_then_decode(pkv, w, gc2, q, kn, vn, last)
+    assert torch.equal(out, two)
+    _same_cache(gc, gc2)
+    oracle.ref_append(cache, w.k[last], w.v[last], w.slot_mapping[last])
+    ref = oracle.ref_decode(q_exact_values(q), cache, w.block_tables, w.context_lens, w.scale,
+                            w.num_q_heads)
+    assert oracle.max_abs_err(to_f64(out), ref) <= 1e-2
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+def test_decode_step_one_byte_many_workgroups(pkv, kv):
+    """Many rounds of workgroups (384 sequences x 12 KV heads, head_dim 64)
+    over a one-byte cache: the separate store launch quantises as the append
+    does; bit for bit the two calls."""
+    from workloads import make_workload
+    say(f"decode step C3 shape stored as {kv}")
+    w = make_workload("C3")
+    _, gc, kn, vn, last = _setup(w, kv, "f32")
+    gc2 = {k: (None if t is None else t.clone()) for k, t in gc.items()}
+    q = q_tensor(w, "f32")
+    out = _fused(pkv, w, gc, q, kn, vn)
+    two = _append_then_decode(pkv, w, gc2, q, kn, vn, last)
+    assert torch.equal(out, two)
+    _same_cache(gc, gc2)
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+def test_decode_step_nan_new_row(pkv, kv):
+    """A NaN in a new K row and in a new V row: both get scale NaN and
+    codes 0 (the append's rule), the heads of those KV heads read NaN, the
+    other rows are untouched; bit for bit the two calls."""
+    ctx = [40, 70, 5, 300]
+    w = small_decode(ctx, 8, 2, 128, kv, seed=730)
+    _, gc, kn, vn, last = _setup(w, kv, "f32")
+    kn[1, 0, 17] = float("nan")
+    vn[3, 1, 100] = float("nan")
+    gc2 = {k: (None if t is None else t.clone()) for k, t in gc.items()}
+    q = q_tensor(w, "f32")
+    out = _fused(pkv, w, gc, q, kn, vn)
+    two = _append_then_decode(pkv, w, gc2, q, kn, vn, last)
+    _same_cache(gc, gc2)
+    o, t = out.cpu().numpy(), two.cpu().numpy()
+    assert np.array_equal(np.isnan(o), np.isnan(t))
+    assert np.all(np.isnan(o[1, :4])) and np.all(np.isnan(o[3, 4:]))
+    fin = np.isfinite(o)
+    assert np.array_equal(o[fin], t[fin])
