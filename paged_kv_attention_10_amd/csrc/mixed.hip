@@ -6,19 +6,21 @@
 // P_b + i and attends to [0, P_b + i]; a decode token is a chunk of one.
 //
 // One launch holds two kinds of workgroups.  The first part of the grid is
-// the prefill kernel's row blocks in grid order (heaviest first); sequences
-// whose chunk is a single token leave them empty, and such a workgroup
-// exits after one load (ranking the sequences first, as the prefill kernel
-// may, measured slower here: every empty workgroup pays for the ranking
-// before the decode partitions behind it can start).  The second part is the decode kernel's
-// partitions, which take exactly those single-token sequences (their query
-// and output rows mapped through cu_q_lens): a decode token is walked by
-// four waves with 16-query-head MFMA tiles instead of occupying a 128-row
-// prefill block.  When the batch holds only short chunks the one-token rows
-// are split across the context as in paged_attn_decode; with long chunks
-// present they take the fewest splits their context allows.  Both kinds share the
+// the prefill row blocks that hold rows, found on the device (see
+// mixed_prefill_item) so that the part is sized by the token count rather
+// than by batch x row blocks, most of which a decode-heavy batch leaves
+// empty.  The second part is the decode kernel's partitions, which take
+// exactly the single-token sequences (their query and output rows mapped
+// through cu_q_lens): a decode token is walked by four waves with
+// 16-query-head MFMA tiles instead of occupying a 128-row prefill block.
+// When the batch holds only short chunks the one-token rows are split
+// across the context as in paged_attn_decode; with long chunks present they
+// take the fewest splits their context allows.  Both kinds share the
 // workgroup's LDS buffer and its register budget; split partials are merged
 // by the decode reduce kernel afterwards.
+
+#include <algorithm>
+
 #include "decode_body.h"
 #include "prefill_body.h"
 
@@ -32,14 +34,74 @@ constexpr int mixed_lds_bytes() {
 
 static_assert(64 * kDecodeWaves == 256, "both kinds of workgroup have 256 threads");
 
+// The prefill part of a mixed launch holds only as many workgroups as row
+// blocks can hold rows (host bound: KV heads x (ceil(tokens x G / 128) +
+// batch), since the chunks' lengths sum to the token count), and each
+// workgroup finds its row block here: the id-th item of the list of row
+// blocks that hold rows, KV head fastest, then the sequences in order, each
+// sequence's row blocks heaviest (last) first.  Every workgroup derives the
+// same list from cu_q_lens with prefix sums of the sequences' row-block
+// counts, 256 sequences per pass.  A workgroup past the list's end gets
+// rb = nrowblocks (no work).  Called by all 256 threads; uses 1 KB of `sh`,
+// free again on return.
+__device__ __forceinline__ void mixed_prefill_item(const PrefillArgs& a, int* sh, int id, int& b,
+                                                   int& g, int& rb) {
+  const int t = threadIdx.x;
+  const int j = id / a.hkv;          // the (sequence, row block) item
+  g = id - j * a.hkv;
+  b = 0;
+  rb = a.nrowblocks;
+  int* scan = sh;                    // [256] inclusive prefix within the pass
+  int* found = sh + 256;             // sequence and row block of item j
+  if (t == 0) found[0] = -1;
+  int base = 0;                      // items before the pass
+  for (int p0 = 0; p0 < a.batch; p0 += 256) {
+    const int s = p0 + t;
+    int n = 0;
+    if (s < a.batch) {
+      // the rows prefill_body gives the sequence (the same clamping)
+      int C = a.cu_q_lens[s + 1] - a.cu_q_lens[s];
+      C = C < 0 ? 0 : min(C, a.max_q_len);
+      const int rows = (a.skip_single && C == 1) ? 0 : C * a.group;
+      n = (rows + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock;
+    }
+    scan[t] = n;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = t >= off ? scan[t - off] : 0;
+      __syncthreads();
+      scan[t] += v;
+      __syncthreads();
+    }
+    const int incl = base + scan[t];
+    if (n > 0 && j >= incl - n && j < incl) {
+      found[0] = s;
+      found[1] = incl - 1 - j;       // heavier (later) row blocks first
+    }
+    base += scan[255];
+    __syncthreads();
+    if (found[0] >= 0 || base > j) break;   // the same in every thread
+  }
+  if (found[0] >= 0) {
+    b = found[0];
+    rb = found[1];
+  }
+  __syncthreads();
+}
+
 template <int D, int KV, bool QSPLIT>
 __global__ __launch_bounds__(256, (prefill_workgroups_per_cu<D, KV>()))
 void mixed_kernel(DecodeArgs da, PrefillArgs pa, int n_prefill) {
   __shared__ __attribute__((aligned(1024))) char lds[mixed_lds_bytes<D, KV>()];
   const int id = blockIdx.x;
   if (id < n_prefill) {
-    const int b = id % pa.batch, r = id / pa.batch;
-    prefill_body<D, KV, QSPLIT>(pa, lds, b, r % pa.hkv, pa.nrowblocks - 1 - r / pa.hkv);
+    // the prefill kernel's ranked order when it applies (at most 256
+    // sequences, contexts that differ, at most two rounds of row blocks),
+    // else the list order
+    int b = 0, g = 0, rb = 0;
+    if (pa.batch > kPrefillSortMaxBatch || !prefill_item(pa, reinterpret_cast<int*>(lds), id, b, g, rb))
+      mixed_prefill_item(pa, reinterpret_cast<int*>(lds), id, b, g, rb);
+    prefill_body<D, KV, QSPLIT>(pa, lds, b, g, rb);
   } else {
     const int j = id - n_prefill;
     const int ny = da.hkv * da.head_tiles;
@@ -202,8 +264,14 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   pa.window = window;
   if (pa.nrowblocks > 65535) return PKV_ERR_INVALID_ARG;
 
-  // no row block can hold work when every chunk has at most one token
-  const long n_prefill = max_q_len > 1 ? (long)batch * num_kv_heads * pa.nrowblocks : 0;
+  // no row block can hold work when every chunk has at most one token;
+  // otherwise at most KV heads x (ceil(tokens x G / 128) + batch) row
+  // blocks hold rows (the chunk lengths sum to num_tokens)
+  const long n_prefill =
+      max_q_len > 1 ? std::min((long)batch * num_kv_heads * pa.nrowblocks,
+                               (long)num_kv_heads * (ceil_div((long)num_tokens * pa.group,
+                                                              kPrefillRowsPerBlock) + batch))
+                    : 0;
   const long n_decode = (long)p.nsplits * num_kv_heads * p.head_tiles * batch;
   if (n_prefill + n_decode > 0x7fffffffL) return PKV_ERR_INVALID_ARG;
 

@@ -126,9 +126,10 @@ constexpr long kPrefillFirstRound = 256;
 constexpr long kPrefillSortMaxGrid = 2 * kPrefillFirstRound;
 
 // `id` is the workgroup's position in the grid order.  Returns false (and
-// leaves b, g, rb alone) when the grid order is kept; a workgroup left
-// without work gets rb = nrowblocks, which prefill_body turns away.  Called
-// by all 256 threads; uses 3 KB of `sh`, free again on return.
+// leaves b, g, rb alone) when the caller's order is kept (also when more
+// than kPrefillSortMaxGrid row blocks hold rows); a workgroup left without
+// work gets rb = nrowblocks, which prefill_body turns away.  Called by all
+// 256 threads; uses 3 KB of `sh`, free again on return.
 __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int* sh, long id, int& b,
                                              int& g, int& rb) {
   const int B = a.batch, H = a.hkv, R = a.nrowblocks;
@@ -168,6 +169,10 @@ __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int* sh, long
   __syncthreads();
   long n_items = 0;
   for (int r = 0; r < B; ++r) n_items += items_of[r];
+  if (n_items > kPrefillSortMaxGrid) {   // more than two rounds: keep the caller's order
+    __syncthreads();
+    return false;
+  }
   if (id >= n_items) {
     rb = R;
   } else {
