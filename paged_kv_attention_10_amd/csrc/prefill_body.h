@@ -507,41 +507,60 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
 
     // one 64-key tile (keys kb .. kb+63; half hf = pages 2hf and 2hf+1)
     run_tiles([&](const char* st, int kb) {
-      // ---- S^T = K * Q^T for both halves: all K fragment reads first (one
-      //      LDS latency), then two independent MFMA chains
-      u32x4 kfr[2][NSTEP];
+      // ---- S^T = K * Q^T for both halves
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      if constexpr (!QSPLIT) {
+        // all K fragment reads first (one LDS latency), then two
+        // independent MFMA chains
+        u32x4 kfr[2][NSTEP];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int k = 0; k < NSTEP; ++k)
+            kfr[hf][k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kaddr[k]);
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k)
-          kfr[hf][k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kaddr[k]);
-      f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int k = 0; k < NSTEP; ++k)
+          for (int hf = 0; hf < 2; ++hf)
+            s[hf] = mfma32x32x16(__builtin_bit_cast(H8, kfr[hf][k]), qhi[k], s[hf]);
+        // keep the K reads ahead of the MFMAs (the default schedule pairs
+        // them and waits for LDS between every two MFMAs)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NSTEP, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NSTEP, 0);
+      } else {
+        // head and remainder of q take 2*NSTEP fragments: one half's K
+        // fragments at a time (two MFMAs per fragment hide the second LDS
+        // latency), so that both halves' fragments are not live together
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const H8 kf = __builtin_bit_cast(H8, kfr[hf][k]);
-          s[hf] = mfma32x32x16(kf, qhi[k], s[hf]);
-          if constexpr (QSPLIT) s[hf] = mfma32x32x16(kf, qlo[k], s[hf]);
-        }
-      // keep the K reads ahead of the MFMAs (the default schedule pairs them
-      // and waits for LDS between every two MFMAs)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NSTEP, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, (QSPLIT ? 4 : 2) * NSTEP, 0);
-      // ---- V^T fragments (their LDS latency hides behind the softmax)
-      u32x4 vfr[2][NDB][2];
+          u32x4 kfr[NSTEP];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+          for (int k = 0; k < NSTEP; ++k)
+            kfr[k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kaddr[k]);
+#pragma unroll
+          for (int k = 0; k < NSTEP; ++k) {
+            const H8 kf = __builtin_bit_cast(H8, kfr[k]);
+            s[hf] = mfma32x32x16(kf, qhi[k], s[hf]);
+            s[hf] = mfma32x32x16(kf, qlo[k], s[hf]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, NSTEP, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NSTEP, 0);
+        }
+      }
+      // ---- V^T fragments of half hf; out-of-range keys may hold anything
+      //      (NaN): their V is zeroed.  Both halves are read here, their
+      //      LDS latency hidden behind the softmax; with a split query (two
+      //      q fragments live) each half is read as its softmax starts, so
+      //      that both halves' fragments are not live together.
+      u32x4 vfr[QSPLIT ? 1 : 2][NDB][2];
+      auto load_v = [&](int hf, u32x4 (&vf)[NDB][2]) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            vfr[hf][db][j] = *reinterpret_cast<const u32x4*>(
+            vf[db][j] = *reinterpret_cast<const u32x4*>(
                 st + vaddr + (2 * hf + j) * L::kPageBytes + db * 32 * 32);
-      // out-of-range keys may hold anything (NaN): zero their V
-      if (edge_tile(kb)) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+        if (edge_tile(kb)) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int key0 = kb + 32 * hf + 16 * j + 8 * hh;
@@ -550,9 +569,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
               const bool out = key0 + e >= ctx || key0 + e < kPage * p_first;
               const uint32_t m = out ? ((e & 1) ? 0x0000ffffu : 0xffff0000u) : 0xffffffffu;
 #pragma unroll
-              for (int db = 0; db < NDB; ++db) vfr[hf][db][j][e >> 1] &= m;
+              for (int db = 0; db < NDB; ++db) vf[db][j][e >> 1] &= m;
             }
           }
+        }
+      };
+      if constexpr (!QSPLIT) {
+        load_v(0, vfr[0]);
+        load_v(1, vfr[QSPLIT ? 0 : 1]);
       }
       // ---- online softmax for query row `col` on raw scores; the
       //      log2e-prescaled scale (positive) is applied inside the
@@ -562,6 +586,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
       float lsum = 0.f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
+        if constexpr (QSPLIT) load_v(hf, vfr[0]);
         H8 p16[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -586,7 +611,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[hf][db][j]), p16[j], acc[db]);
+            acc[db] = mfma32x32x16(__builtin_bit_cast(H8, vfr[QSPLIT ? 0 : hf][db][j]), p16[j], acc[db]);
       }
       l_part += lsum;
     });
@@ -668,33 +693,61 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     const int saddr = L::sOff + 128 * hh;
 
     run_tiles([&](const char* st, int kb) {
-      // ---- S^T = K * Q^T: the lane's K chunks of both halves, then the MFMAs
-      u32x4 kfr[2][KCH];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int i = 0; i < KCH; ++i)
-          kfr[hf][i] = *reinterpret_cast<const u32x4*>(st + hf * 2 * L::kPageBytes + kaddr[i]);
+      // ---- S^T = K * Q^T: the lane's K chunks of both halves, then the
+      //      MFMAs (with a split query one half at a time, so that both
+      //      halves' chunks are not live together)
       f32x16 s[2] = {f32x16{}, f32x16{}};
+      auto qk_half = [&](int hf, const u32x4 (&kf4)[KCH]) {
 #pragma unroll
-      for (int k = 0; k < NSTEP; ++k)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const u32x4 w = kfr[hf][k >> 1];
+        for (int k = 0; k < NSTEP; ++k) {
+          const u32x4 w = kf4[k >> 1];
           const u32x2 codes = (k & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
           const f16x8 kf = codes8_to_f16<KV>(codes);
           s[hf] = mfma32x32x16(kf, qhi[k], s[hf]);
           if constexpr (QSPLIT) s[hf] = mfma32x32x16(kf, qlo[k], s[hf]);
         }
-      // ---- V^T codes (16 keys of one d row of the lane's page per half)
-      //      and that page's scales
-      u32x4 vfr[2][NDB];
+      };
+      if constexpr (!QSPLIT) {
+        u32x4 kfr[2][KCH];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int i = 0; i < KCH; ++i)
+            kfr[hf][i] = *reinterpret_cast<const u32x4*>(st + hf * 2 * L::kPageBytes + kaddr[i]);
+#pragma unroll
+        for (int k = 0; k < NSTEP; ++k)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const u32x4 w = kfr[hf][k >> 1];
+            const u32x2 codes = (k & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+            s[hf] = mfma32x32x16(codes8_to_f16<KV>(codes), qhi[k], s[hf]);
+          }
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          u32x4 kfr[KCH];
+#pragma unroll
+          for (int i = 0; i < KCH; ++i)
+            kfr[i] = *reinterpret_cast<const u32x4*>(st + hf * 2 * L::kPageBytes + kaddr[i]);
+          qk_half(hf, kfr);
+        }
+      }
+      // ---- V^T codes (16 keys of one d row of the lane's page per half;
+      //      with a split query read per half in the PV loop) and that
+      //      page's scales
+      u32x4 vfr[QSPLIT ? 1 : 2][NDB];
+      auto load_v = [&](int hf, u32x4 (&vf)[NDB]) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          vf[db] = *reinterpret_cast<const u32x4*>(st + vaddr + hf * 2 * L::kPageBytes + db * 32 * 16);
+      };
+      if constexpr (!QSPLIT) {
+        load_v(0, vfr[0]);
+        load_v(1, vfr[QSPLIT ? 0 : 1]);
+      }
       f32x4 ksc[2][4], vsc[2][4];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          vfr[hf][db] = *reinterpret_cast<const u32x4*>(st + vaddr + hf * 2 * L::kPageBytes + db * 32 * 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ksc[hf][i] = *reinterpret_cast<const f32x4*>(st + saddr + 256 * hf + 16 * i);
@@ -719,8 +772,13 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         const int nv = key0 < kPage * p_first ? 0 : ctx - key0;   // in-range keys of the page
 #pragma unroll
         for (int r = 0; r < 16; ++r) vs[hf][r] = (!edge || r < nv) ? vsc[hf][r >> 2][r & 3] : 0.f;
+      }
+      // FP8 codes of out-of-range keys zeroed (the NaN codes)
+      auto mask_codes = [&](int hf, u32x4 (&vf)[NDB]) {
         if constexpr (KV == PKV_FP8) {
           if (edge) {
+            const int key0 = kb + 32 * hf + 16 * hh;
+            const int nv = key0 < kPage * p_first ? 0 : ctx - key0;
             u32x4 m;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -728,10 +786,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
               m[q] = n >= 4 ? 0xffffffffu : ((1u << (8 * n)) - 1u);
             }
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) vfr[hf][db] &= m;
+            for (int db = 0; db < NDB; ++db) vf[db] &= m;
           }
         }
-      }
+      };
       float vmax = 0.f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
@@ -749,6 +807,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
       float lsum = 0.f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
+        if constexpr (QSPLIT) load_v(hf, vfr[0]);
+        u32x4 (&vf)[NDB] = vfr[QSPLIT ? 0 : hf];
+        mask_codes(hf, vf);
         f16x8 p16[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -759,8 +820,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         // ---- O^T += V^T * P^T: keys 0-7 of the page, then 8-15
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const f16x8 v0 = codes8_to_f16<KV>(u32x2{vfr[hf][db][0], vfr[hf][db][1]});
-          const f16x8 v1 = codes8_to_f16<KV>(u32x2{vfr[hf][db][2], vfr[hf][db][3]});
+          const f16x8 v0 = codes8_to_f16<KV>(u32x2{vf[db][0], vf[db][1]});
+          const f16x8 v1 = codes8_to_f16<KV>(u32x2{vf[db][2], vf[db][3]});
           acc[db] = mfma32x32x16(v0, p16[0], acc[db]);
           acc[db] = mfma32x32x16(v1, p16[1], acc[db]);
         }
