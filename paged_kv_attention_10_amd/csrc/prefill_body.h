@@ -62,12 +62,17 @@ struct PrefillArgs {
 // then (int8 / FP8) each page's 16 K scales and 16 V scales.
 template <int D, int KV>
 struct PrefillLds {
-  static constexpr int ES = KV == PKV_F32 ? 4 : (kv_code8(KV) ? 1 : 2);   // bytes per element
+  // bytes per element in LDS: fp32 caches 4, the others 2 (one-byte codes
+  // are converted to fp16 as the tile is staged)
+  static constexpr int ES = KV == PKV_F32 ? 4 : 2;
   static constexpr int kRow = ES * D;                // bytes of one K row
   static constexpr int kPageBytes = kPage * kRow;    // one page of K (= one page of V^T)
   static constexpr int vOff = 4 * kPageBytes;        // V^T blocks after the 64 K rows
-  static constexpr int sOff = 8 * kPageBytes;        // per page: 16 K scales, 16 V scales
-  static constexpr int stage = 8 * kPageBytes + (kv_code8(KV) ? 4 * 128 : 0);
+  // one-byte caches: per page 16 K scales and 16 V scales, then the four
+  // pages' largest in-range V scale
+  static constexpr int sOff = 8 * kPageBytes;
+  static constexpr int pmOff = sOff + 4 * 128;
+  static constexpr int stage = 8 * kPageBytes + (kv_code8(KV) ? 1024 : 0);
   static constexpr int dmaPerPage = kPageBytes / 1024;
 };
 
@@ -93,16 +98,6 @@ constexpr int prefill_workgroups_per_cu() {
 // a 16-lane read (64 bytes apart) in 16 different 16-byte bank slots.
 __device__ __forceinline__ int k_swizzle32(int rr) { return (rr ^ ((rr & 8) >> 1)) & 15; }
 __device__ __forceinline__ int v_swizzle32(int d) { return ((d >> 2) ^ (d >> 1)) & 3; }
-
-// The same for one-byte K rows (D bytes), which also depends on the parity
-// p of the page in the tile: a 16-lane fragment read touches rows 0-7 or
-// 8-15 of two neighbouring pages, and these slots put its 16 chunks in 16
-// different 16-byte bank slots (and any 8 lanes of it in 8 of 128 bytes).
-template <int D>
-__device__ __forceinline__ int k_swizzle8(int p, int rr) {
-  if constexpr (D == 128) return ((rr ^ (rr >> 2)) & 3) | (p << 2);
-  else return (((rr >> 1) ^ (rr >> 2)) & 1) | (p << 1);
-}
 
 constexpr float kLazyRescale = 8.0f;
 
@@ -209,23 +204,21 @@ __device__ __forceinline__ f16x8 codes8_to_f16(u32x2 w) {
 // One row block: the 128 rows rb of (sequence b, KV head g).  Called by all
 // 256 threads of the workgroup; `lds` holds two tile stages (1024-aligned).
 //
-// int8 / FP8 caches: the tile's codes and scales are copied as they lie and
-// each wave converts the codes it reads to fp16, exactly (int8 with the
-// v_perm + subtract trick, FP8 with the hardware convert).  The query row is
-// scaled by the power of two 2^e that puts its largest magnitude in
-// [2^14, 2^15) and rounded to fp16 (split into head + remainder for an fp32
-// query); a bf16 or fp16 query is then exact down to 2^-32 of that largest
-// magnitude.  The scores take the K scale and c * 2^-e.  The V scale
-// multiplies the probability (0 * anything = 0 there, so a NaN scale of a
-// masked key stays out), normalised per wave as in the decode: scales are
-// multiplied by 2^(4 - v_exp), v_exp the binade of the largest in-range
-// scale met so far, raised (with the accumulator scaled down to match) when
-// a tile's largest scale lies more than two binades above it, so p * scale
-// stays below 2^14 in fp16; the power of two goes back on at the end.  The
-// A-operand row of S^T reads another key than in the 16-bit case: lane
-// (c + 32*h) then holds, for query row c, the scores of all 16 keys of page
-// 2*hf + h of the tile (register r: key r), so one 16-byte V^T read covers
-// both PV k-steps of a half and a lane's scales are one page's.
+// int8 / FP8 caches: each tile's codes are converted once, exactly, to fp16
+// as the tile is staged in LDS (int8 with the v_perm + subtract trick, FP8
+// with the hardware convert), so the compute reads fp16 fragments as the
+// 16-bit path does.  The query row is scaled by the power of two 2^e that
+// puts its largest magnitude in [2^14, 2^15) and rounded to fp16 (split
+// into head + remainder for an fp32 query); a bf16 or fp16 query is then
+// exact down to 2^-32 of that largest magnitude.  The scores take the K
+// scale and c * 2^-e.  The V scale multiplies the probability (0 * anything
+// = 0 there, so a NaN scale of a masked key stays out), normalised as in
+// the decode: scales are multiplied by 2^(4 - v_exp), v_exp the binade of
+// the largest in-range scale met so far (the same in every wave: each tile
+// stages its pages' largest scales), raised (with the accumulator scaled
+// down to match) when a tile's largest scale lies more than two binades
+// above it, so p * scale stays below 2^14 in fp16; the power of two goes
+// back on at the end.
 template <int D, int KV, bool QSPLIT>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, int b, int g, int rb) {
   constexpr bool kI8 = kv_code8(KV);
@@ -236,7 +229,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   using L = PrefillLds<D, KV>;
   constexpr int NSTEP = D / 16;  // QK k-steps of 16
   constexpr int NDB = D / 32;    // 32-row blocks of d for PV
-  constexpr int KCH = D / 32;    // one-byte K: 16-byte chunks per lane and half
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -280,9 +272,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   const int npages = (ctx + kPage - 1) / kPage;
   const long qrow = ((long)(q0 + pos) * a.hq + h) * D;
 
-  // ---- Q^T fragments (B operand), column col.  16-bit caches: k-chunk
-  //      d = 16*s + 8*hh; one-byte caches: d = (D/2)*hh + 8*s, so that a
-  //      lane's K codes for its k-steps are one contiguous run of its row.
+  // ---- Q^T fragments (B operand), column col, k-chunk d = 16*s + 8*hh.
   //      A query in the cache's own 16-bit type is used as it is; otherwise
   //      the row goes through fp32 (times the sign of the scale) and, when
   //      the MFMA takes fp16, is scaled by the power of two 2^e that puts its
@@ -320,7 +310,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
       uint32_t bits[NSTEP][8];
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s)
-        io_bits_vec<8, QT>(a.q, qrow + (kI8 ? (D / 2) * hh + 8 * s : 16 * s + 8 * hh), bits[s]);
+        io_bits_vec<8, QT>(a.q, qrow + 16 * s + 8 * hh, bits[s]);
       float x[NSTEP][8];
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s)
@@ -370,37 +360,44 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   int pid_cur = load_window(t_first >> 4);
   int pid_next = ntiles > (t_first | 15) + 1 ? load_window((t_first >> 4) + 1) : 0;
 
-  // ---- tile copy: wave w moves page 4t + w of the tile (K rows swizzled,
-  //      V^T block as is, and for one-byte caches the page's 16 K and 16 V
-  //      scales, lanes 0-3 and 4-7) into stage `stg`; pages past the context
-  //      are not read (their keys are masked and their V is zeroed or
-  //      weighted by zero)
-  const char* kc = static_cast<const char*>(a.k_cache);
-  const char* vc = static_cast<const char*>(a.v_cache);
-  int koff[L::dmaPerPage];
-#pragma unroll
-  for (int j = 0; j < L::dmaPerPage; ++j) {
-    const int byte = 1024 * j + 16 * lane;          // position inside the page's K block
-    const int rr = byte / L::kRow, slot = (byte % L::kRow) / 16;
-    if constexpr (kI8) koff[j] = rr * L::kRow + ((slot ^ k_swizzle8<D>(wave & 1, rr)) * 16);
-    else if constexpr (kF32) koff[j] = rr * L::kRow + ((slot ^ k_swizzle32(rr & 15)) * 16);
-    else koff[j] = rr * L::kRow + ((slot ^ k_swizzle<D>(rr)) * 16);
-  }
-  // fp32 V^T rows are 64 bytes: the swizzle of row d = 16*j + lane/4 does
-  // not depend on j
-  const int voff = kF32 ? 64 * (lane >> 2) + (((lane & 3) ^ v_swizzle32(lane >> 2)) * 16) : 16 * lane;
-  const char* sc_src = nullptr;
-  if constexpr (kI8)
-    sc_src = reinterpret_cast<const char*>(lane < 4 ? a.k_scales : a.v_scales) + 16 * (lane & 3);
-  auto issue_tile = [&](int t, int stg) {
+  // ---- page id of page 4t + w of tile t for wave w (the page-id window
+  //      advanced every 16 tiles; called once per tile, in order), or -1
+  //      for a page not read (past the context, or wholly before the
+  //      window: its keys are masked and its V zeroed or weighted by zero)
+  auto tile_page = [&](int t) {
     if ((t & 15) == 0 && t > t_first) {
       pid_cur = pid_next;
       pid_next = load_window((t >> 4) + 1);
     }
     const int pi = 4 * t + wave;
-    if (pi < npages && pi >= p_first) {
-      int pid = __builtin_amdgcn_readlane(pid_cur, pi & 63);
-      if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
+    if (pi >= npages || pi < p_first) return -1;
+    int pid = __builtin_amdgcn_readlane(pid_cur, pi & 63);
+    if ((unsigned)pid >= (unsigned)a.num_pages) { bad = true; pid = 0; }
+    return pid;
+  };
+
+  // ---- tile copy (16- and 32-bit caches): wave w moves page 4t + w of the
+  //      tile (K rows swizzled, V^T block as is) into stage `stg` with LDS
+  //      DMA
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  int koff[kI8 ? 1 : L::dmaPerPage];
+  int voff = 16 * lane;
+  if constexpr (!kI8) {
+#pragma unroll
+    for (int j = 0; j < L::dmaPerPage; ++j) {
+      const int byte = 1024 * j + 16 * lane;          // position inside the page's K block
+      const int rr = byte / L::kRow, slot = (byte % L::kRow) / 16;
+      if constexpr (kF32) koff[j] = rr * L::kRow + ((slot ^ k_swizzle32(rr & 15)) * 16);
+      else koff[j] = rr * L::kRow + ((slot ^ k_swizzle<D>(rr)) * 16);
+    }
+    // fp32 V^T rows are 64 bytes: the swizzle of row d = 16*j + lane/4 does
+    // not depend on j
+    if constexpr (kF32) voff = 64 * (lane >> 2) + (((lane & 3) ^ v_swizzle32(lane >> 2)) * 16);
+  }
+  auto issue_tile = [&](int t, int stg) {
+    const int pid = tile_page(t);
+    if (pid >= 0) {
       const long blk = ((long)pid * a.hkv + g) * L::kPageBytes;
       char* lk = lds + stg * L::stage + wave * L::kPageBytes;
       char* lv = lds + stg * L::stage + L::vOff + wave * L::kPageBytes;
@@ -408,10 +405,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
       for (int j = 0; j < L::dmaPerPage; ++j) {
         dma16(kc + blk + koff[j], lk + 1024 * j);
         dma16(vc + blk + 1024 * j + voff, lv + 1024 * j);
-      }
-      if constexpr (kI8) {
-        if (lane < 8)
-          dma16(sc_src + ((long)pid * a.hkv + g) * (kPage * 4), lds + stg * L::stage + L::sOff + 128 * wave);
       }
     }
   };
@@ -679,123 +672,132 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         }
     });
   } else {
-    // per-lane LDS offsets: the A-operand row col of S^T reads key
-    // 16*((col/4)&1) + 4*(col/8) + col%4 of the half (page (col/4)&1), its
-    // k-chunks (D/32)*hh .. (D/32)*hh + D/32 - 1; V^T row d = col of the
-    // half's page hh (+ 32*db)
-    const int key = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
-    const int kp = key >> 4, krr = key & 15;
-    int kaddr[KCH];
+    // ---- one-byte caches.  Wave w loads the codes of page 4t + w of the
+    //      next tile into registers (lane l: D/4 bytes of the K page and of
+    //      the V^T page; lanes 0-7 the page's 16 K and 16 V scales) while the
+    //      current tile computes, then converts them, each code once, to
+    //      fp16 in the next stage in the 16-bit layout (K rows swizzled, V^T
+    //      rows as they are), zeroes the V of keys past the context or before
+    //      the window, stores the scales (those keys' V scales as 0) and the
+    //      page's largest V scale.  The compute reads fp16 fragments as the
+    //      16-bit path does; register r of half hf holds key
+    //      32*hf + 16*(r/8) + 8*hh + r%8, i.e. key 8*hh + r%8 of page
+    //      2*hf + r/8.
+    constexpr int KQ = D / 64;                      // 16-byte code chunks per lane and page
+    struct Codes {
+      u32x4 k[KQ], v[KQ], sc;
+    };
+    const char* sc_src =
+        reinterpret_cast<const char*>(lane < 4 ? a.k_scales : a.v_scales) + 16 * (lane & 3);
+    auto load_codes = [&](int t, Codes& c) {
+      const int pid = tile_page(t);
+      if (pid >= 0) {
+        const long blk = ((long)pid * a.hkv + g) * (long)(kPage * D);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i)
-      kaddr[i] = kp * L::kPageBytes + krr * L::kRow + ((((D / 32) * hh + i) ^ k_swizzle8<D>(kp, krr)) * 16);
-    const int vaddr = L::vOff + hh * L::kPageBytes + col * 16;
-    const int saddr = L::sOff + 128 * hh;
+        for (int i = 0; i < KQ; ++i) {
+          c.k[i] = *reinterpret_cast<const u32x4*>(kc + blk + 16 * (KQ * lane + i));
+          c.v[i] = *reinterpret_cast<const u32x4*>(vc + blk + 16 * (KQ * lane + i));
+        }
+        if (lane < 8)
+          c.sc = *reinterpret_cast<const u32x4*>(sc_src + ((long)pid * a.hkv + g) * (kPage * 4));
+      }
+    };
+    auto stage_codes = [&](int t, int stg, const Codes& c) {
+      char* F = lds + stg * L::stage;
+      // in-range keys of the page (none for a page not read)
+      const int pi = 4 * t + wave;
+      const int nv = (pi >= npages || pi < p_first) ? 0 : min(max(ctx - kPage * pi, 0), kPage);
+      // K row lane/4 of the page, d = (D/4)*(lane%4) ..: 2*KQ fp16 chunks
+      const int kr = lane >> 2;
+      char* krow = F + wave * L::kPageBytes + kr * L::kRow;
+#pragma unroll
+      for (int i = 0; i < KQ; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ch = 2 * KQ * (lane & 3) + 2 * i + h;
+          *reinterpret_cast<f16x8*>(krow + ((ch ^ k_swizzle<D>(kr)) * 16)) =
+              codes8_to_f16<KV>(u32x2{c.k[i][2 * h], c.k[i][2 * h + 1]});
+        }
+      // V^T row KQ*lane + i (16 keys), keys at or past nv zeroed
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) {
+        f16x8 lo = codes8_to_f16<KV>(u32x2{c.v[i][0], c.v[i][1]});
+        f16x8 hi = codes8_to_f16<KV>(u32x2{c.v[i][2], c.v[i][3]});
+        if (nv < kPage) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (e >= nv) lo[e] = (_Float16)0.f;
+            if (8 + e >= nv) hi[e] = (_Float16)0.f;
+          }
+        }
+        char* vrow = F + L::vOff + wave * L::kPageBytes + (KQ * lane + i) * 32;
+        *reinterpret_cast<f16x8*>(vrow) = lo;
+        *reinterpret_cast<f16x8*>(vrow + 16) = hi;
+      }
+      // scales: lanes 0-3 the K scales of keys 4*lane.., lanes 4-7 the V
+      // scales of keys 4*(lane-4)..; the page's largest in-range V scale
+      float pm = 0.f;
+      if (lane < 8) {
+        f32x4 x = __builtin_bit_cast(f32x4, c.sc);
+        if (lane >= 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (4 * (lane - 4) + e >= nv) x[e] = 0.f;
+            pm = fmaxf(pm, x[e]);
+          }
+        }
+        *reinterpret_cast<f32x4*>(F + L::sOff + 128 * wave + 16 * lane) = x;
+      }
+      pm = fmaxf(pm, __shfl_xor(pm, 1));
+      pm = fmaxf(pm, __shfl_xor(pm, 2));
+      if (lane == 4) reinterpret_cast<float*>(F + L::pmOff)[wave] = pm;
+    };
 
-    run_tiles([&](const char* st, int kb) {
-      // ---- S^T = K * Q^T: the lane's K chunks of both halves, then the
-      //      MFMAs (with a split query one half at a time, so that both
-      //      halves' chunks are not live together)
+    // K fragment k of this lane: row krow, chunk (2k + hh) ^ swz (the swizzle
+    // is below 16, so it only flips the low bits of the chunk index)
+    const int kbase = krow * L::kRow;
+    const int kswz = k_swizzle<D>(krow & 15);
+    const int vaddr = L::vOff + col * 32 + hh * 16;
+    const int saddr = L::sOff + 32 * hh;
+
+    auto compute_tile = [&](const char* st, int kb) {
+      // ---- S^T = K * Q^T, one half at a time
       f32x16 s[2] = {f32x16{}, f32x16{}};
-      auto qk_half = [&](int hf, const u32x4 (&kf4)[KCH]) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 kfr[NSTEP];
+#pragma unroll
+        for (int k = 0; k < NSTEP; ++k)
+          kfr[k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kbase +
+                                                   (((2 * k + hh) ^ kswz) * 16));
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k) {
-          const u32x4 w = kf4[k >> 1];
-          const u32x2 codes = (k & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
-          const f16x8 kf = codes8_to_f16<KV>(codes);
+          const f16x8 kf = __builtin_bit_cast(f16x8, kfr[k]);
           s[hf] = mfma32x32x16(kf, qhi[k], s[hf]);
           if constexpr (QSPLIT) s[hf] = mfma32x32x16(kf, qlo[k], s[hf]);
         }
-      };
-      if constexpr (!QSPLIT) {
-        u32x4 kfr[2][KCH];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int i = 0; i < KCH; ++i)
-            kfr[hf][i] = *reinterpret_cast<const u32x4*>(st + hf * 2 * L::kPageBytes + kaddr[i]);
-#pragma unroll
-        for (int k = 0; k < NSTEP; ++k)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const u32x4 w = kfr[hf][k >> 1];
-            const u32x2 codes = (k & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
-            s[hf] = mfma32x32x16(codes8_to_f16<KV>(codes), qhi[k], s[hf]);
-          }
-      } else {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          u32x4 kfr[KCH];
-#pragma unroll
-          for (int i = 0; i < KCH; ++i)
-            kfr[i] = *reinterpret_cast<const u32x4*>(st + hf * 2 * L::kPageBytes + kaddr[i]);
-          qk_half(hf, kfr);
-        }
+        __builtin_amdgcn_sched_group_barrier(0x100, NSTEP, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (QSPLIT ? 2 : 1) * NSTEP, 0);
       }
-      // ---- V^T codes (16 keys of one d row of the lane's page per half;
-      //      with a split query read per half in the PV loop) and that
-      //      page's scales
-      u32x4 vfr[QSPLIT ? 1 : 2][NDB];
-      auto load_v = [&](int hf, u32x4 (&vf)[NDB]) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          vf[db] = *reinterpret_cast<const u32x4*>(st + vaddr + hf * 2 * L::kPageBytes + db * 32 * 16);
-      };
-      if constexpr (!QSPLIT) {
-        load_v(0, vfr[0]);
-        load_v(1, vfr[QSPLIT ? 0 : 1]);
-      }
-      f32x4 ksc[2][4], vsc[2][4];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ksc[hf][i] = *reinterpret_cast<const f32x4*>(st + saddr + 256 * hf + 16 * i);
-          vsc[hf][i] = *reinterpret_cast<const f32x4*>(st + saddr + 256 * hf + 64 + 16 * i);
-        }
-      }
-      // ---- scores in log2 units; register r of half hf holds key
-      //      kb + 32*hf + 16*hh + r
+      // ---- scores in log2 units: K scale times c * 2^-e
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[hf][r] *= ksc[hf][r >> 2][r & 3] * row_c;
-      apply_masks(s, kb, [&](int hf) { return 32 * hf + 16 * hh; }, [](int r) { return r; });
+        for (int j = 0; j < 2; ++j) {
+          const char* sp = st + saddr + 128 * (2 * hf + j);
+          const f32x4 k0 = *reinterpret_cast<const f32x4*>(sp);
+          const f32x4 k1 = *reinterpret_cast<const f32x4*>(sp + 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[hf][8 * j + e] *= k0[e] * row_c;
+            s[hf][8 * j + 4 + e] *= k1[e] * row_c;
+          }
+        }
+      apply_masks(s, kb, base16, roff16);
       const float m_use = update_max(tile_max(s));
-      // ---- V scales: out-of-range keys may hold anything (scales and, for
-      //      FP8, NaN codes): their scale is taken as 0 and their codes zeroed
-      const bool edge = edge_tile(kb);
-      float vs[2][16];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int key0 = kb + 32 * hf + 16 * hh;
-        const int nv = key0 < kPage * p_first ? 0 : ctx - key0;   // in-range keys of the page
-#pragma unroll
-        for (int r = 0; r < 16; ++r) vs[hf][r] = (!edge || r < nv) ? vsc[hf][r >> 2][r & 3] : 0.f;
-      }
-      // FP8 codes of out-of-range keys zeroed (the NaN codes)
-      auto mask_codes = [&](int hf, u32x4 (&vf)[NDB]) {
-        if constexpr (KV == PKV_FP8) {
-          if (edge) {
-            const int key0 = kb + 32 * hf + 16 * hh;
-            const int nv = key0 < kPage * p_first ? 0 : ctx - key0;
-            u32x4 m;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int n = min(max(nv - 4 * q, 0), 4);
-              m[q] = n >= 4 ? 0xffffffffu : ((1u << (8 * n)) - 1u);
-            }
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) vf[db] &= m;
-          }
-        }
-      };
-      float vmax = 0.f;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, vs[hf][r]);
-      vmax = max_xor32(vmax);
+      // ---- V normaliser from the four pages' largest in-range V scales
+      const f32x4 pm = *reinterpret_cast<const f32x4*>(st + L::pmOff);
+      const float vmax = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
       const int et = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(vmax));
       if (et > v_exp + 2) {
 #pragma unroll
@@ -804,30 +806,50 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
           for (int r = 0; r < 16; ++r) acc[i][r] = __builtin_ldexpf(acc[i][r], v_exp - et);
         v_exp = et;
       }
+      // ---- P (times the normalised V scale) and O^T += V^T * P^T, one
+      //      16-key page at a time
       float lsum = 0.f;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        if constexpr (QSPLIT) load_v(hf, vfr[0]);
-        u32x4 (&vf)[NDB] = vfr[QSPLIT ? 0 : hf];
-        mask_codes(hf, vf);
-        f16x8 p16[2];
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[hf][r] - m_use);
-          lsum += p;
-          p16[r >> 3][r & 7] = (_Float16)mul_zero_wins(p, __builtin_ldexpf(vs[hf][r], 4 - v_exp));
-        }
-        // ---- O^T += V^T * P^T: keys 0-7 of the page, then 8-15
+        for (int j = 0; j < 2; ++j) {
+          u32x4 vfr[NDB];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const f16x8 v0 = codes8_to_f16<KV>(u32x2{vf[db][0], vf[db][1]});
-          const f16x8 v1 = codes8_to_f16<KV>(u32x2{vf[db][2], vf[db][3]});
-          acc[db] = mfma32x32x16(v0, p16[0], acc[db]);
-          acc[db] = mfma32x32x16(v1, p16[1], acc[db]);
+          for (int db = 0; db < NDB; ++db)
+            vfr[db] = *reinterpret_cast<const u32x4*>(
+                st + vaddr + (2 * hf + j) * L::kPageBytes + db * 32 * 32);
+          const char* sp = st + saddr + 128 * (2 * hf + j) + 64;
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(sp);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(sp + 16);
+          f16x8 p16;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(s[hf][8 * j + e] - m_use);
+            lsum += p;
+            const float vsc = e < 4 ? v0[e] : v1[e - 4];
+            p16[e] = (_Float16)mul_zero_wins(p, __builtin_ldexpf(vsc, 4 - v_exp));
+          }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32x32x16(__builtin_bit_cast(f16x8, vfr[db]), p16, acc[db]);
         }
-      }
       l_part += lsum;
-    });
+    };
+
+    // ---- pipeline: tile t computes from one stage while tile t+1's codes
+    //      are in flight to registers; they are staged into the other stage
+    //      after the compute, one barrier per tile
+    Codes cr = {};
+    load_codes(t_first, cr);
+    stage_codes(t_first, t_first & 1, cr);
+    __syncthreads();
+    for (int t = t_first; t < ntiles; ++t) {
+      const bool more = t + 1 < ntiles;
+      if (more) load_codes(t + 1, cr);
+      compute_tile(lds + (t & 1) * L::stage, t * kPrefillTileKeys);
+      if (more) stage_codes(t + 1, (t + 1) & 1, cr);
+      __syncthreads();
+    }
   }
   bad = __syncthreads_or(bad);
 
