@@ -84,6 +84,12 @@ __device__ __forceinline__ int k_swizzle(int rr) {
   else return (rr ^ (rr >> 3)) & 7;
 }
 
+// 16-bit V^T rows (16 keys, two 16-byte chunks): chunk c of row d is
+// stored in slot c ^ v_swizzle16(d).  A fragment read has lanes c .. c+15
+// on rows d .. d+15 and one chunk: without the swap rows d and d + 8 share
+// a 16-byte bank slot (a two-way conflict in every 16-lane group).
+__device__ __forceinline__ int v_swizzle16(int d) { return (d >> 3) & 1; }
+
 // Workgroups a CU can hold for this stage size (160 KB of LDS per CU): two
 // for the 16-bit and one-byte caches, one for fp32 at head_dim 128.
 template <int D, int KV>
@@ -382,7 +388,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
   int koff[kI8 ? 1 : L::dmaPerPage];
-  int voff = 16 * lane;
+  // lane l's V^T chunk of a 1 KB block: row l/2 of the block, the chunk
+  // that lands in slot l%2
+  int voff = 32 * (lane >> 1) + 16 * ((lane & 1) ^ v_swizzle16(lane >> 1));
   if constexpr (!kI8) {
 #pragma unroll
     for (int j = 0; j < L::dmaPerPage; ++j) {
@@ -496,7 +504,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k)
       kaddr[k] = krow * L::kRow + (((2 * k + hh) ^ k_swizzle<D>(krow & 15)) * 16);
-    const int vaddr = L::vOff + col * 32 + hh * 16;
+    const int vaddr = L::vOff + col * 32 + 16 * (hh ^ v_swizzle16(col));
 
     // one 64-key tile (keys kb .. kb+63; half hf = pages 2hf and 2hf+1)
     run_tiles([&](const char* st, int kb) {
