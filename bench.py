@@ -381,7 +381,9 @@ def bench_prefill(g: Gpu, steps: int, warmup: int, name: str = "C4"):
         # counters are taken for the bf16 batch only
         res["roofline"] = {"bound": "mfma", "achieved": res["tflops_prefill_call"],
                            "peak": peak, "unit": "TFLOP/s",
-                           "frac": res["tflops_prefill_call"] / peak, "traffic": None}
+                           "frac": res["tflops_prefill_call"] / peak,
+                           "traffic": profiled_traffic(f"prefill_{name}_counters.txt",
+                                                       source_sha("prefill.hip", "prefill_body.h", "pkv_device.h", "pkv_host.h"))}
         return w, res, out
     res["roofline"] = {"bound": "mfma", "achieved": res["tflops_prefill_call"],
                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
