@@ -66,6 +66,11 @@ constexpr int kDecodeMaxTilesPerSplit = 32 * kDecodeWaves;
 constexpr int kDecodeMaxSplits = 64;
 // Longest context a decode call takes.
 constexpr long kDecodeMaxContext = (long)kDecodeMaxSplits * kDecodeMaxTilesPerSplit * kDecodeTileTokens;
+// A split takes at least two tiles per wave: a call of a few short
+// contexts (a handful of sequences of a few hundred tokens) then runs as
+// one split per sequence and skips the merge launch, which costs more than
+// the splits would save.
+constexpr int kDecodeMinTilesPerSplit = 2 * kDecodeWaves;
 // Aim for about this many workgroups per call: one per CU of a 256-CU
 // MI355X.  Fewer, longer splits measured faster than more, shorter ones:
 // every split pays a few dependent memory round trips before its first
@@ -103,7 +108,7 @@ inline DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int 
   if (want < 1) want = 1;
   int tps = ceil_div(tiles_max, want);
   tps = ceil_div(tps, kDecodeWaves) * kDecodeWaves;
-  if (tps < kDecodeWaves) tps = kDecodeWaves;
+  if (tps < kDecodeMinTilesPerSplit) tps = kDecodeMinTilesPerSplit;
   if (tps > kDecodeMaxTilesPerSplit) tps = kDecodeMaxTilesPerSplit;
   p.tiles_per_split = tps;
   p.nsplits = ceil_div(tiles_max, tps);   // <= kDecodeMaxSplits for spans <= kDecodeMaxContext
