@@ -681,17 +681,25 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     });
   } else {
     // ---- one-byte caches.  Wave w loads the codes of page 4t + w of the
-    //      next tile into registers (lane l: D/4 bytes of the K page and of
-    //      the V^T page; lanes 0-7 the page's 16 K and 16 V scales) while the
-    //      current tile computes, then converts them, each code once, to
-    //      fp16 in the next stage in the 16-bit layout (K rows swizzled, V^T
-    //      rows as they are), zeroes the V of keys past the context or before
+    //      next tile into registers (lane l: D/4 bytes of the K page and two
+    //      V^T rows, see kVSwap; lanes 0-7 the page's 16 K and 16 V scales)
+    //      while the current tile computes, then converts them, each code
+    //      once, to fp16 in the next stage in the 16-bit layout (K rows
+    //      swizzled, V^T row halves swapped), zeroes the V of keys past the context or before
     //      the window, stores the scales (those keys' V scales as 0) and the
     //      page's largest V scale.  The compute reads fp16 fragments as the
     //      16-bit path does; register r of half hf holds key
     //      32*hf + 16*(r/8) + 8*hh + r%8, i.e. key 8*hh + r%8 of page
     //      2*hf + r/8.
     constexpr int KQ = D / 64;                      // 16-byte code chunks per lane and page
+    // Lane l stages V^T rows l and l + 64 with their halves swapped as in
+    // the 16-bit layout (staging writes and fragment reads free of bank
+    // conflicts), except with a split query, whose kernel keeps rows 2l and
+    // 2l + 1 unswapped: measured, the conflict-free layout speeds the
+    // 16-bit-query kernels up by 4-6% and slows the split-query ones (at
+    // 256 VGPRs) by 7%
+    constexpr bool kVSwap = !QSPLIT;
+    auto vrow_of = [&](int i) { return kVSwap ? lane + 64 * i : KQ * lane + i; };
     struct Codes {
       u32x4 k[KQ], v[KQ], sc;
     };
@@ -704,7 +712,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
 #pragma unroll
         for (int i = 0; i < KQ; ++i) {
           c.k[i] = *reinterpret_cast<const u32x4*>(kc + blk + 16 * (KQ * lane + i));
-          c.v[i] = *reinterpret_cast<const u32x4*>(vc + blk + 16 * (KQ * lane + i));
+          c.v[i] = *reinterpret_cast<const u32x4*>(vc + blk + 16 * vrow_of(i));
         }
         if (lane < 8)
           c.sc = *reinterpret_cast<const u32x4*>(sc_src + ((long)pid * a.hkv + g) * (kPage * 4));
@@ -726,7 +734,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
           *reinterpret_cast<f16x8*>(krow + ((ch ^ k_swizzle<D>(kr)) * 16)) =
               codes8_to_f16<KV>(u32x2{c.k[i][2 * h], c.k[i][2 * h + 1]});
         }
-      // V^T row KQ*lane + i (16 keys), keys at or past nv zeroed
+      // V^T row vrow_of(i) (16 keys), keys at or past nv zeroed, its two
+      // 16-byte halves swapped as the 16-bit copy swaps them (kVSwap): the
+      // 16 lanes of a write then cover 16 different bank slots
 #pragma unroll
       for (int i = 0; i < KQ; ++i) {
         f16x8 lo = codes8_to_f16<KV>(u32x2{c.v[i][0], c.v[i][1]});
@@ -738,9 +748,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
             if (8 + e >= nv) hi[e] = (_Float16)0.f;
           }
         }
-        char* vrow = F + L::vOff + wave * L::kPageBytes + (KQ * lane + i) * 32;
-        *reinterpret_cast<f16x8*>(vrow) = lo;
-        *reinterpret_cast<f16x8*>(vrow + 16) = hi;
+        const int vd = vrow_of(i);
+        char* vrow = F + L::vOff + wave * L::kPageBytes + vd * 32;
+        const int vsw = kVSwap ? v_swizzle16(vd) : 0;
+        *reinterpret_cast<f16x8*>(vrow + 16 * vsw) = lo;
+        *reinterpret_cast<f16x8*>(vrow + 16 * (1 ^ vsw)) = hi;
       }
       // scales: lanes 0-3 the K scales of keys 4*lane.., lanes 4-7 the V
       // scales of keys 4*(lane-4)..; the page's largest in-range V scale
@@ -765,7 +777,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     // is below 16, so it only flips the low bits of the chunk index)
     const int kbase = krow * L::kRow;
     const int kswz = k_swizzle<D>(krow & 15);
-    const int vaddr = L::vOff + col * 32 + hh * 16;
+    const int vaddr = L::vOff + col * 32 + 16 * (kVSwap ? (hh ^ v_swizzle16(col)) : hh);
     const int saddr = L::sOff + 32 * hh;
 
     auto compute_tile = [&](const char* st, int kb) {
