@@ -452,8 +452,9 @@ def bench_ceiling(g: Gpu, sizes, steps: int, warmup: int):
     """The practical streaming-read ceiling: libpkv_probe.so's read-only
     kernel (hand-written HIP, outside the library, see csrc/probe.hip)
     reads `nbytes` of a 1 GiB device buffer once, after the same 1 GiB
-    flush as every timed call, HIP events on the stream it runs on.  Three
-    grid sizes; the fastest is reported, labelled as a measured probe."""
+    flush as every timed call, HIP events on the stream it runs on.  Five
+    grid sizes (256 to 4096 workgroups); the fastest is reported, labelled
+    as a measured probe."""
     import ctypes
     torch = g.torch
     lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_attention_10_amd", "libpkv_probe.so"))
@@ -467,7 +468,7 @@ def bench_ceiling(g: Gpu, sizes, steps: int, warmup: int):
     for nbytes in sizes:
         nbytes = min(int(nbytes) // 16 * 16, buf.numel())
         best = None
-        for wg in (1024, 2048, 4096):
+        for wg in (256, 512, 1024, 2048, 4096):
             ms = []
             for i in range(warmup + steps):
                 g.flush()
@@ -489,7 +490,7 @@ def bench_ceiling(g: Gpu, sizes, steps: int, warmup: int):
         res.append(best)
     return {"kind": "measured streaming-read probe (read-only HIP kernel outside the library, "
                     "16-byte non-temporal loads, cold after the 1 GiB flush); median of the timed "
-                    "calls, fastest of 1024/2048/4096 workgroups",
+                    "calls, fastest of 256/512/1024/2048/4096 workgroups",
             "reads": res}
 
 
