@@ -29,6 +29,28 @@ __device__ __forceinline__ void dma16(const void* g, void* l) {
                                    (__attribute__((address_space(3))) void*)l, 16, 0, 0);
 }
 
+// The same copy issued from inline asm: the compiler does not count it among
+// its vector-memory operations, so it neither waits for it before LDS reads
+// of the other stage (it cannot tell the stages apart) nor keeps it out of a
+// run of MFMAs.  The copy has no register result and reads its address
+// registers when it issues; M0 carries the LDS address (the compiler sets
+// M0 again before any use of its own).  Its caller waits for it with
+// wait_vmcnt0 before the barrier that hands the stage to the other waves;
+// the compiler's own vector-memory waits stay correct (a copy it does not
+// count only makes them wait longer).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved: nothing else keeps a value in it here
+__device__ __forceinline__ void dma16_async(const void* g, void* l) {
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)l;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(la)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// s_waitcnt vmcnt(0) with the other counters unbounded
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRowsPerBlock = kPrefillRowsPerWave * kPrefillWaves;
@@ -403,17 +425,19 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     // not depend on j
     if constexpr (kF32) voff = 64 * (lane >> 2) + (((lane & 3) ^ v_swizzle32(lane >> 2)) * 16);
   }
+  // part j of the copy of page pid into stage stg: K and V^T chunks j
+  auto copy_part = [&](int pid, int stg, int j) {
+    const long blk = ((long)pid * a.hkv + g) * L::kPageBytes;
+    char* lk = lds + stg * L::stage + wave * L::kPageBytes;
+    char* lv = lds + stg * L::stage + L::vOff + wave * L::kPageBytes;
+    dma16_async(kc + blk + koff[j], lk + 1024 * j);
+    dma16_async(vc + blk + 1024 * j + voff, lv + 1024 * j);
+  };
   auto issue_tile = [&](int t, int stg) {
     const int pid = tile_page(t);
     if (pid >= 0) {
-      const long blk = ((long)pid * a.hkv + g) * L::kPageBytes;
-      char* lk = lds + stg * L::stage + wave * L::kPageBytes;
-      char* lv = lds + stg * L::stage + L::vOff + wave * L::kPageBytes;
 #pragma unroll
-      for (int j = 0; j < L::dmaPerPage; ++j) {
-        dma16(kc + blk + koff[j], lk + 1024 * j);
-        dma16(vc + blk + 1024 * j + voff, lv + 1024 * j);
-      }
+      for (int j = 0; j < L::dmaPerPage; ++j) copy_part(pid, stg, j);
     }
   };
 
@@ -427,15 +451,25 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
   // ---- pipeline: tile t computes from LDS while tile t+1 is copied in
   auto run_tiles = [&](auto&& compute_tile) {
     issue_tile(t_first, t_first & 1);
-    __syncthreads();  // waits for this wave's copies, then for every wave's
+    wait_vmcnt0();
+    __syncthreads();  // this wave's copies have landed; now every wave's
     for (int t = t_first; t < ntiles; ++t) {
-      if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
       const char* st = lds + (t & 1) * L::stage;
       const int kb = t * kPrefillTileKeys;
       // every wave computes every tile: a tile past all of a wave's rows is
       // fully masked (p = 0), and branching around it would make the compiler
-      // copy the accumulators at each join
-      compute_tile(st, kb);
+      // copy the accumulators at each join.  compute_tile calls issue_next
+      // (the copy of tile t+1 into the other stage) where the copies' issue
+      // best overlaps its own work.
+      // The copy is unconditional (no branch between it and the MFMAs it
+      // is interleaved with): a page not read, or the tile after the last,
+      // copies page 0 instead, into a stage whose keys are then masked
+      // (their V zeroed) or never computed on.  issue_next(j) issues part j
+      // of L::dmaPerPage.
+      const int pid_next = max(tile_page(t + 1), 0);
+      auto issue_next = [&](int j) { copy_part(pid_next, (t + 1) & 1, j); };
+      compute_tile(st, kb, issue_next);
+      wait_vmcnt0();
       __syncthreads();
     }
   };
@@ -507,28 +541,37 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     const int vaddr = L::vOff + col * 32 + 16 * (hh ^ v_swizzle16(col));
 
     // one 64-key tile (keys kb .. kb+63; half hf = pages 2hf and 2hf+1)
-    run_tiles([&](const char* st, int kb) {
+    run_tiles([&](const char* st, int kb, auto&& issue_next) {
       // ---- S^T = K * Q^T for both halves
       f32x16 s[2] = {f32x16{}, f32x16{}};
       if constexpr (!QSPLIT) {
         // all K fragment reads first (one LDS latency), then two
-        // independent MFMA chains
+        // independent MFMA chains; the next tile's copies are issued while
+        // the K reads are in flight
         u32x4 kfr[2][NSTEP];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int k = 0; k < NSTEP; ++k)
             kfr[hf][k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kaddr[k]);
+        // keep the K reads ahead of the MFMAs (the default schedule pairs
+        // them and waits for LDS between every two MFMAs); the next tile's
+        // copies go in pairs after the first MFMA pairs, issued while the
+        // matrix core runs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k = 0; k < NSTEP; ++k)
+        for (int k = 0; k < NSTEP; ++k) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf)
             s[hf] = mfma32x32x16(__builtin_bit_cast(H8, kfr[hf][k]), qhi[k], s[hf]);
-        // keep the K reads ahead of the MFMAs (the default schedule pairs
-        // them and waits for LDS between every two MFMAs)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NSTEP, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NSTEP, 0);
+          if (k < L::dmaPerPage) {
+            issue_next(k);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       } else {
+#pragma unroll
+        for (int j = 0; j < L::dmaPerPage; ++j) issue_next(j);
         // head and remainder of q take 2*NSTEP fragments: one half's K
         // fragments at a time (two MFMAs per fragment hide the second LDS
         // latency), so that both halves' fragments are not live together
@@ -625,7 +668,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     const int ksw = k_swizzle32(krow & 15);
     const int vsw = v_swizzle32(col);          // the swizzle of row 32*db + col
     const int vrow = L::vOff + col * 64;
-    run_tiles([&](const char* st, int kb) {
+    run_tiles([&](const char* st, int kb, auto&& issue_next) {
+#pragma unroll
+      for (int j = 0; j < L::dmaPerPage; ++j) issue_next(j);
       // ---- S^T = K * Q^T, the two halves' MFMA chains interleaved
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
