@@ -825,8 +825,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     const int vaddr = L::vOff + col * 32 + 16 * (kVSwap ? (hh ^ v_swizzle16(col)) : hh);
     const int saddr = L::sOff + 32 * hh;
 
-    auto compute_tile = [&](const char* st, int kb) {
-      // ---- S^T = K * Q^T, one half at a time
+    auto compute_tile = [&](const char* st, int kb, auto&& issue_next) {
+      // ---- S^T = K * Q^T, one half at a time; the next tile's code loads
+      //      are issued while the first half's K reads are in flight
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -835,6 +836,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
         for (int k = 0; k < NSTEP; ++k)
           kfr[k] = *reinterpret_cast<const u32x4*>(st + hf * 32 * L::kRow + kbase +
                                                    (((2 * k + hh) ^ kswz) * 16));
+        if (hf == 0) issue_next();
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k) {
           const f16x8 kf = __builtin_bit_cast(f16x8, kfr[k]);
@@ -910,8 +912,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* lds, in
     __syncthreads();
     for (int t = t_first; t < ntiles; ++t) {
       const bool more = t + 1 < ntiles;
-      if (more) load_codes(t + 1, cr);
-      compute_tile(lds + (t & 1) * L::stage, t * kPrefillTileKeys);
+      compute_tile(lds + (t & 1) * L::stage, t * kPrefillTileKeys, [&]() {
+        if (more) load_codes(t + 1, cr);
+      });
       if (more) stage_codes(t + 1, (t + 1) & 1, cr);
       __syncthreads();
     }
