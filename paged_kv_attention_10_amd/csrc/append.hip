@@ -151,23 +151,48 @@ __device__ void query_block(const AppendArgs& a, long qb, double2* cs) {
   constexpr int NSEG = D / kSegElems;
   const int tpb = a.q_tokens_per_block;
   const long tok0 = qb * tpb;
-  build_rope_table<D>(a, tok0, tpb, cs);
-  __syncthreads();
   const int segs = a.hq * NSEG;
   const int es = a.q_dtype == PKV_F32 ? 4 : 2;
-  for (int t = threadIdx.x; t < tpb * segs; t += kAppendThreads) {
-    const int lt = t / segs;
-    const long tok = tok0 + lt;
-    if (tok >= a.num_tokens) continue;
+  const bool split = a.style == PKV_ROPE_HALF;
+  // item t: token lt, head h, segment s; its row and first column
+  auto item = [&](int t, int& lt, int& s, char*& row, int& c0, int& c1) {
+    lt = t / segs;
     const int rem = t - lt * segs;
-    const int h = rem / NSEG, s = rem - h * NSEG;
-    const bool split = a.style == PKV_ROPE_HALF;
-    const int c0 = split ? 8 * s : kSegElems * s;
-    const int c1 = split ? D / 2 + 8 * s : kSegElems * s + 8;
-    char* row = static_cast<char*>(a.q) + (tok * a.hq + h) * D * es;
+    const int h = rem / NSEG;
+    s = rem - h * NSEG;
+    c0 = split ? 8 * s : kSegElems * s;
+    c1 = split ? D / 2 + 8 * s : kSegElems * s + 8;
+    row = static_cast<char*>(a.q) + ((tok0 + lt) * a.hq + h) * D * es;
+  };
+  // the first pass's query segment is loaded before the angle table is
+  // built (the same memory round trip as the positions)
+  const int t_first = threadIdx.x;
+  float x0[16];
+  uint32_t raw0[16];
+  if (t_first < tpb * segs && tok0 + t_first / segs < a.num_tokens) {
+    int lt, s, c0, c1;
+    char* row;
+    item(t_first, lt, s, row, c0, c1);
+    load8x2(row, a.q_dtype, c0, c1, x0, raw0);
+  }
+  build_rope_table<D>(a, tok0, tpb, cs);
+  __syncthreads();
+  for (int t = t_first; t < tpb * segs; t += kAppendThreads) {
+    int lt, s, c0, c1;
+    char* row;
+    item(t, lt, s, row, c0, c1);
+    if (tok0 + lt >= a.num_tokens) continue;
     float x[16];
     uint32_t raw[16];
-    load8x2(row, a.q_dtype, c0, c1, x, raw);
+    if (t == t_first) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        x[j] = x0[j];
+        raw[j] = raw0[j];
+      }
+    } else {
+      load8x2(row, a.q_dtype, c0, c1, x, raw);
+    }
     rotate16(x, raw, cs + lt * (D / 2) + 8 * s, split);
     store8(row, a.q_dtype, c0, x, raw);
     store8(row, a.q_dtype, c1, x + 8, raw + 8);
@@ -187,6 +212,36 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
   constexpr int NSEG = D / kSegElems;
   const int tpb = a.kv_tokens_per_block;
   const long tok0 = kb * tpb;
+  const int segs = 2 * a.hkv * NSEG;
+  const int items = tpb * segs;
+  // item t: token lt, row (K heads, then V heads), 16-element segment s
+  auto item = [&](int t, int& lt, int& row, int& s) {
+    lt = t / segs;
+    const int rem = t - lt * segs;
+    row = rem / NSEG;
+    s = rem - row * NSEG;
+  };
+  auto seg_cols = [&](int row, int s, int& c0, int& c1) {
+    const bool split = ROPE && row < a.hkv && a.style == PKV_ROPE_HALF;
+    c0 = split ? 8 * s : kSegElems * s;
+    c1 = split ? D / 2 + 8 * s : kSegElems * s + 8;
+  };
+  auto load_item = [&](int t, float* x, uint32_t* raw) {
+    int lt, row, s, c0, c1;
+    item(t, lt, row, s);
+    seg_cols(row, s, c0, c1);
+    const bool is_v = row >= a.hkv;
+    const int h = is_v ? row - a.hkv : row;
+    const char* src = static_cast<const char*>(is_v ? a.v_new : a.k_new) +
+                      ((tok0 + lt) * a.hkv + h) * D * (a.new_dtype == PKV_F32 ? 4 : 2);
+    load8x2(src, a.new_dtype, c0, c1, x, raw);
+  };
+  // the first pass's input segment does not depend on the slot: loaded
+  // before the barrier, in the same memory round trip as the slots
+  float x0[16];
+  uint32_t raw0[16];
+  const int t_first = threadIdx.x;
+  if (t_first < items && tok0 + t_first / segs < a.num_tokens) load_item(t_first, x0, raw0);
   if (threadIdx.x < tpb) {
     const long tok = tok0 + threadIdx.x;
     int64_t slot = tok < a.num_tokens ? a.slots[tok] : -1;
@@ -196,30 +251,32 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
   if (ROPE) build_rope_table<D>(a, tok0, tpb, cs);
   __syncthreads();
 
-  const int segs = 2 * a.hkv * NSEG;
   const int ces = a.cache_dtype == PKV_F32 ? 4 : kv_scaled(a.cache_dtype) ? 1 : 2;
-  for (int t = threadIdx.x; t < tpb * segs; t += kAppendThreads) {
+  for (int t = t_first; t < items; t += kAppendThreads) {
     // a row's NSEG lanes are consecutive and aligned and share a token, so
     // the int8 shuffle stays inside a group of lanes active together
-    const int lt = t / segs;
+    int lt, row, s, c0, c1;
+    item(t, lt, row, s);
     const int64_t slot = s_slot[lt];
     if (slot < 0) continue;
-    const long tok = tok0 + lt;
-    const int rem = t - lt * segs;
-    const int row = rem / NSEG, s = rem - row * NSEG;
+    seg_cols(row, s, c0, c1);
     const bool is_v = row >= a.hkv;
     const int h = is_v ? row - a.hkv : row;
     const long page = slot / kPage;
     const int off = (int)(slot - page * kPage);
     const bool rotate = ROPE && !is_v;
     const bool split = rotate && a.style == PKV_ROPE_HALF;
-    const int c0 = split ? 8 * s : kSegElems * s;
-    const int c1 = split ? D / 2 + 8 * s : kSegElems * s + 8;
-    const char* src = static_cast<const char*>(is_v ? a.v_new : a.k_new) +
-                      (tok * a.hkv + h) * D * (a.new_dtype == PKV_F32 ? 4 : 2);
     float x[16];
     uint32_t raw[16];
-    load8x2(src, a.new_dtype, c0, c1, x, raw);
+    if (t == t_first) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        x[j] = x0[j];
+        raw[j] = raw0[j];
+      }
+    } else {
+      load_item(t, x, raw);
+    }
     if (rotate) rotate16(x, raw, cs + lt * (D / 2) + 8 * s, split);
 
     const long head = page * a.hkv + h;
@@ -297,13 +354,17 @@ __device__ void kv_block(const AppendArgs& a, long kb, double2* cs, unsigned cha
 // Its chain per token is short and its waves spread over many CUs, which
 // beats the segment kernel's LDS staging below a few thousand (token, head)
 // rows.  No RoPE (that path shares angle tables across a token's heads).
+// The lane's D/64 elements of one new row: values and storage bits (an
+// fp32 input keeps its bits).
 template <int D>
-__device__ __forceinline__ void row_append(const AppendArgs& a, const void* src, void* cache,
-                                           float* scales, long row, long page, int off, int g,
-                                           bool is_v, int lane) {
+struct RowIn {
+  float x[D / 64];
+  uint32_t raw[D / 64];
+};
+template <int D>
+__device__ __forceinline__ RowIn<D> load_row(const AppendArgs& a, const void* src, long row, int lane) {
   constexpr int PER = D / 64;
-  float x[PER];
-  uint32_t raw[PER];
+  RowIn<D> r;
   with_io_dtype(a.new_dtype, [&](auto ndt) {
     constexpr int NT = decltype(ndt)::value;
     uint32_t bits[PER];
@@ -311,10 +372,19 @@ __device__ __forceinline__ void row_append(const AppendArgs& a, const void* src,
     for (int e = 0; e < PER; ++e) bits[e] = io_bits<NT>(src, row * D + lane * PER + e);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      x[e] = io_value<NT>(bits[e]);
-      raw[e] = NT == PKV_F32 ? bits[e] : __float_as_uint(x[e]);
+      r.x[e] = io_value<NT>(bits[e]);
+      r.raw[e] = NT == PKV_F32 ? bits[e] : __float_as_uint(r.x[e]);
     }
   });
+  return r;
+}
+template <int D>
+__device__ __forceinline__ void row_append(const AppendArgs& a, const RowIn<D>& in, void* cache,
+                                           float* scales, long page, int off, int g, bool is_v,
+                                           int lane) {
+  constexpr int PER = D / 64;
+  const float* x = in.x;
+  const uint32_t* raw = in.raw;
   const long head = page * a.hkv + g;
   auto dst_index = [&](int d) -> long {
     return is_v ? (head * D + d) * kPage + off : (head * kPage + off) * D + d;
@@ -348,13 +418,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_rows_kernel(AppendArgs 
   if (w >= (long)a.num_tokens * a.hkv) return;
   const long tok = w / a.hkv;
   const int g = (int)(w - tok * a.hkv);
+  const long row = tok * a.hkv + g;
+  // the new rows do not depend on the slot: loaded in the same memory round
+  // trip as it
+  const RowIn<D> kin = load_row<D>(a, a.k_new, row, lane);
+  const RowIn<D> vin = load_row<D>(a, a.v_new, row, lane);
   const int64_t slot = a.slots[tok];
   if (slot < 0 || slot >= a.num_slots) return;
   const long page = slot / kPage;
   const int off = (int)(slot - page * kPage);
-  const long row = tok * a.hkv + g;
-  row_append<D>(a, a.k_new, a.k_cache, a.k_scales, row, page, off, g, false, lane);
-  row_append<D>(a, a.v_new, a.v_cache, a.v_scales, row, page, off, g, true, lane);
+  row_append<D>(a, kin, a.k_cache, a.k_scales, page, off, g, false, lane);
+  row_append<D>(a, vin, a.v_cache, a.v_scales, page, off, g, true, lane);
 }
 
 // (token, KV head) rows up to which a plain append takes the row kernel.
