@@ -205,7 +205,9 @@ int paged_kv_append_rope(const void* k_new, const void* v_new, int new_dtype,
  * ratio, keys spanning up to 262144 tokens (the whole context, or with a
  * window the window; PKV_ERR_UNSUPPORTED beyond).  Long contexts are split
  * into partitions whose softmax partials are merged with their log-sum-exp
- * weights by a second kernel on the same stream.
+ * weights: inside the launch, by the partition that finishes last, when the
+ * plan has at most eight partitions per sequence, else by a second kernel
+ * on the same stream.
  */
 int paged_attn_decode(const void* q, int q_dtype,
                       const void* k_cache, const void* v_cache,
@@ -274,7 +276,8 @@ int paged_attn_decode_append(const void* q, int q_dtype,
  * nothing.  Every call on one GPU shares that GPU's buffer: calls that may
  * overlap in time (on different streams) race and must be serialised by the
  * caller.  Nothing in the buffer needs clearing between calls: each call
- * writes every partial it reads.
+ * writes every partial it reads, and its merge counters carry the call's
+ * own tag.
  */
 #define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
 

@@ -14,10 +14,15 @@
 // max / sum / accumulator (the max updated lazily: the accumulator is
 // rescaled only when it grows by more than 2^8); the four waves merge in
 // LDS.  A sequence whose context needs several splits writes normalised
-// partials and a log2-sum-exp per split, merged by decode_reduce_kernel on
-// the same stream (the kernel boundary makes the partials visible across
-// the XCDs' separate L2 caches, which an in-kernel merge would have to
-// write back and invalidate).
+// partials and a log2-sum-exp per split.  With at most kMergeInKernelSplits
+// splits the split that finishes last merges them inside the launch: the
+// partials go out as agent-coherent stores (visible across the XCDs'
+// separate L2 caches without writing back or invalidating a whole L2, which
+// a fenced version did and measured 3-7x slower), each split counts itself
+// in on an epoch-tagged arrival counter once its stores have completed, and
+// the last reads the partials back with agent-coherent loads.  Longer plans
+// merge with decode_reduce_kernel on the same stream, whose one-wave-per-row
+// grid reads many splits in one round trip.
 //
 // Fused decode step (paged_attn_decode_append).  The wave whose tiles hold
 // position ctx - 1 loads the sequence's new K/V row with its first tiles,
@@ -100,7 +105,7 @@ static void launch_decode(const DecodeArgs& a, pkv_stream_t stream) {
   else
     hipLaunchKernelGGL((decode_partition_kernel<D, KV, true>), grid, dim3(64 * kDecodeWaves), 0,
                        (hipStream_t)stream, a);
-  if (a.nsplits > 1)
+  if (a.nsplits > 1 && !a.merge_cnt)
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.hq, a.batch), dim3(64), 0,
                        (hipStream_t)stream, a);
 }
@@ -127,7 +132,7 @@ extern "C" size_t paged_attn_decode_workspace_bytes(int batch, int num_q_heads, 
       !decode_span_supported(max_context_len, window))
     return 0;
   DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, window);
-  return decode_workspace_layout(batch, num_q_heads, head_dim, p).total;
+  return decode_workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, p, true).total;
 }
 
 // Checks and launch shared by paged_attn_decode and paged_attn_decode_append
@@ -161,7 +166,7 @@ static int decode_call(const void* q, int q_dtype, const void* k_cache, const vo
     return PKV_ERR_MISALIGNED;
 
   DecodePlan p = plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, window);
-  DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, head_dim, p);
+  DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, p, true);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (workspace && !aligned16(workspace)) return PKV_ERR_MISALIGNED;
 
@@ -178,6 +183,10 @@ static int decode_call(const void* q, int q_dtype, const void* k_cache, const vo
   char* wsb = static_cast<char*>(workspace);
   a.part_o = ws.total ? reinterpret_cast<float*>(wsb + ws.part_o_offset) : nullptr;
   a.part_lse = ws.total ? reinterpret_cast<float*>(wsb + ws.part_lse_offset) : nullptr;
+  a.merge_cnt = ws.total && p.nsplits <= kMergeInKernelSplits
+                    ? reinterpret_cast<unsigned long long*>(wsb + ws.cnt_offset)
+                    : nullptr;
+  a.epoch = next_merge_epoch();
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
   a.max_blocks = max_blocks_per_seq;

@@ -24,6 +24,13 @@ struct DecodeArgs {
   void* out;
   float* part_o;
   float* part_lse;
+  // In-kernel merge (null: the partials go to decode_reduce_kernel): one
+  // arrival counter per (sequence, KV head x head tile), tagged with the
+  // call's epoch (distinct per call) in its upper 56 bits, so that whatever
+  // a counter held before (an earlier call's count, or anything at all in a
+  // fresh workspace) reads as no arrivals yet.
+  unsigned long long* merge_cnt = nullptr;
+  unsigned long long epoch = 0;
   int q_dtype, out_dtype;
   int max_blocks, max_context_len;
   int batch, hq, hkv, group, head_tiles, num_pages;
@@ -810,9 +817,89 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
       store_from_f32(a.out, ((long)qb * a.hq + h0 + hc) * D + d, a.out_dtype, val);
     } else {
       const long prow = row * a.nsplits + split;
-      a.part_o[prow * D + d] = val;
-      if (d == 0) a.part_lse[prow] = poison ? NAN : (den > 0.f ? M + log2f(den) : -INFINITY);
+      const float lse = poison ? NAN : (den > 0.f ? M + log2f(den) : -INFINITY);
+      if (a.merge_cnt) {
+        // agent-coherent stores: the sequence's other splits, on any XCD,
+        // read them with agent-coherent loads
+        __hip_atomic_store(&a.part_o[prow * D + d], val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) __hip_atomic_store(&a.part_lse[prow], lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        a.part_o[prow * D + d] = val;
+        if (d == 0) a.part_lse[prow] = lse;
+      }
     }
+  }
+  if (direct || !a.merge_cnt) return;
+
+  // ---- in-kernel merge: every split waits until its own partial stores
+  //      have completed (agent-coherent, so visible to every XCD), then
+  //      counts itself in with an atomic on the (sequence, gy) counter; the
+  //      split that arrives last reads all nsplit_b partials back with
+  //      agent-coherent loads and writes the output, as decode_reduce_kernel
+  //      does (log-sum-exp weights, NaN from a poisoned split).  Completed
+  //      stores before the counter, and the counter's returned value before
+  //      the loads, order the two sides.  The counter goes from any value
+  //      of another epoch to (epoch, 1) and then counts up: a compare-and-
+  //      swap loop that fails only when another split counted in first, so
+  //      it ends within nsplit_b + 1 tries.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are done
+  __syncthreads();
+  int* const s_last = s_bad + 1;
+  if (threadIdx.x == 0) {
+    unsigned long long* cnt = a.merge_cnt + (long)b * (a.hkv * a.head_tiles) + gy;
+    unsigned long long cur = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long want = 0;
+    bool done = false;
+    for (int it = 0; it <= kDecodeMaxSplits + 1 && !done; ++it) {
+      want = ((cur >> 8) == a.epoch ? cur : (a.epoch << 8)) + 1;
+      done = __hip_atomic_compare_exchange_strong(cnt, &cur, want, __ATOMIC_RELAXED,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *s_last = done && (int)(want & 0xff) == nsplit_b;
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  for (int idx = threadIdx.x; idx < nh * D; idx += 64 * kDecodeWaves) {
+    const int hc = idx / D, d = idx - hc * D;
+    const long row = (long)b * a.hq + h0 + hc;
+    // eight splits' lse and element per round trip, folded into a running
+    // log-sum-exp
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    bool nan_in = false;
+    for (int s0 = 0; s0 < nsplit_b; s0 += 8) {
+      float l8[8], o8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const long prow = row * a.nsplits + s0 + k;
+        const bool in = s0 + k < nsplit_b;
+        l8[k] = in ? __hip_atomic_load(&a.part_lse[prow], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : -INFINITY;
+        o8[k] = in ? __hip_atomic_load(&a.part_o[prow * D + d], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0.f;
+      }
+      float m8 = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        nan_in |= l8[k] != l8[k];
+        m8 = fmaxf(m8, l8[k]);
+      }
+      if (m8 != -INFINITY) {
+        const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - m8);
+        num *= r;
+        den *= r;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float w = l8[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l8[k] - m8);
+          num += o8[k] * w;
+          den += w;
+        }
+        M = m8;
+      }
+    }
+    float val = den > 0.f ? num / den : 0.f;
+    if (!ctx_ok || nan_in) val = NAN;
+    store_from_f32(a.out, ((long)qb * a.hq + h0 + hc) * D + d, a.out_dtype, val);
   }
 }
 

@@ -17,7 +17,8 @@
 // across the context as in paged_attn_decode; with long chunks present they
 // take the fewest splits their context allows.  Both kinds share the
 // workgroup's LDS buffer and its register budget; split partials are merged
-// by the decode reduce kernel afterwards.
+// as in a decode call (inside the launch by the last split for plans of up
+// to eight splits, else by the decode reduce kernel afterwards).
 
 #include <algorithm>
 
@@ -122,7 +123,7 @@ static void launch_mixed(const DecodeArgs& da, const PrefillArgs& pa, int n_pref
   else
     hipLaunchKernelGGL((mixed_kernel<D, KV, false>), grid, dim3(256), 0, (hipStream_t)stream, da, pa,
                        n_prefill);
-  if (da.nsplits > 1)
+  if (da.nsplits > 1 && !da.merge_cnt)
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(da.hq, da.batch), dim3(64), 0,
                        (hipStream_t)stream, da);
 }
@@ -142,7 +143,7 @@ static void dispatch_mixed(int kv, const DecodeArgs& da, const PrefillArgs& pa, 
 // Split plan of the one-token rows.  With long chunks in the batch
 // (max_q_len >= kMixedLongChunk) the prefill row blocks set the critical
 // path, so the one-token rows take the fewest splits their context allows (a
-// split would only add the merge launch); otherwise the one-token rows
+// split would only add the merge); otherwise the one-token rows
 // dominate and are planned as a decode call.
 constexpr int kMixedLongChunk = 128;
 static DecodePlan mixed_plan(int batch, int num_q_heads, int num_kv_heads, int max_q_len,
@@ -163,9 +164,10 @@ extern "C" size_t paged_attn_mixed_workspace_bytes(int batch, int num_q_heads, i
       !head_dim_built(head_dim) || max_q_len < 0 || max_context_len < 0 || window < 0 ||
       !decode_span_supported(max_context_len, window))
     return 0;
-  return decode_workspace_layout(batch, num_q_heads, head_dim,
+  return decode_workspace_layout(batch, num_q_heads, num_kv_heads, head_dim,
                                  mixed_plan(batch, num_q_heads, num_kv_heads, max_q_len,
-                                            max_context_len, window)).total;
+                                            max_context_len, window),
+                                 true).total;
 }
 
 extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
@@ -198,7 +200,7 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   if (num_tokens == 0 || max_q_len == 0) return PKV_OK;
 
   const DecodePlan p = mixed_plan(batch, num_q_heads, num_kv_heads, max_q_len, max_context_len, window);
-  const DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, head_dim, p);
+  const DecodeWorkspace ws = decode_workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, p, true);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (workspace && !aligned16(workspace)) return PKV_ERR_MISALIGNED;
 
@@ -215,6 +217,12 @@ extern "C" int paged_attn_mixed(const void* q, int q_dtype, const void* k_cache,
   char* wsb = static_cast<char*>(workspace);
   da.part_o = ws.total ? reinterpret_cast<float*>(wsb + ws.part_o_offset) : nullptr;
   da.part_lse = ws.total ? reinterpret_cast<float*>(wsb + ws.part_lse_offset) : nullptr;
+  // decode rows merge as in a decode call: inside the launch for plans of up
+  // to kMergeInKernelSplits splits, else with the reduce kernel
+  da.merge_cnt = ws.total && p.nsplits <= kMergeInKernelSplits
+                     ? reinterpret_cast<unsigned long long*>(wsb + ws.cnt_offset)
+                     : nullptr;
+  da.epoch = next_merge_epoch();
   da.q_dtype = q_dtype;
   da.out_dtype = out_dtype;
   da.max_blocks = max_blocks_per_seq;

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "../../include/pkv.h"
@@ -117,21 +118,39 @@ inline DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int 
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Plans of up to this many splits merge inside the partition launch (the
+// last split reads every partial in one round trip of eight); longer ones
+// use decode_reduce_kernel.  C2 (two splits): fused step 44.5 -> 42.7 us; a
+// 16k-64k-token plan of many splits measured 1.4% slower merged in-kernel.
+constexpr int kMergeInKernelSplits = 8;
+
+// Epochs of the in-kernel merge's arrival counters: distinct for every call
+// in the process (56 bits).
+inline unsigned long long next_merge_epoch() {
+  static std::atomic<unsigned long long> epoch{1};
+  return epoch.fetch_add(1, std::memory_order_relaxed) & ((1ull << 56) - 1);
+}
+
 // Workspace of a split decode: normalised partial outputs and their
 // log2-sum-exp, [batch][num_q_heads][nsplits] rows.  Contents on entry do
 // not matter.
+// Split partials (o, then lse) and, for the in-kernel merge, one 64-bit
+// arrival counter per (sequence, KV head x head tile).
 struct DecodeWorkspace {
-  size_t part_o_offset, part_lse_offset, total;
+  size_t part_o_offset, part_lse_offset, cnt_offset, total;
 };
 
-inline DecodeWorkspace decode_workspace_layout(int batch, int num_q_heads, int head_dim,
-                                               const DecodePlan& p) {
-  DecodeWorkspace w = {0, 0, 0};
+inline DecodeWorkspace decode_workspace_layout(int batch, int num_q_heads, int num_kv_heads,
+                                               int head_dim, const DecodePlan& p,
+                                               bool merge_counters) {
+  DecodeWorkspace w = {0, 0, 0, 0};
   if (p.nsplits <= 1) return w;
   size_t rows = (size_t)batch * num_q_heads * p.nsplits;
   w.part_o_offset = 0;
   w.part_lse_offset = align_up(rows * head_dim * sizeof(float), 256);
-  w.total = w.part_lse_offset + align_up(rows * sizeof(float), 256);
+  w.cnt_offset = w.part_lse_offset + align_up(rows * sizeof(float), 256);
+  w.total = w.cnt_offset +
+            (merge_counters ? align_up((size_t)batch * num_kv_heads * p.head_tiles * 8, 256) : 0);
   return w;
 }
 

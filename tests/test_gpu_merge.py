@@ -1,8 +1,9 @@
 """GPU tests of the split merge: decodes whose contexts need several splits
-write per-split partials and log2-sum-exps to the workspace, merged by the
-reduce kernel.  One workspace serves calls of any shape, a bad page id in
-one split poisons only its sequence, and a large batch with a few long
-contexts splits only those."""
+write per-split partials and log2-sum-exps to the workspace, merged inside
+the launch by the split that finishes last (plans of up to eight splits) or
+by the reduce kernel.  One workspace serves calls of any shape and any
+initial contents, a bad page id in one split poisons only its sequence, and
+a large batch with a few long contexts splits only those."""
 import numpy as np
 import pytest
 import torch
@@ -95,3 +96,30 @@ def test_merge_propagates_nan(pkv):
     ref = oracle.ref_decode(q_exact_values(q), c, w.block_tables, w.context_lens, w.scale, 12)
     keep = [0, 2, 3]
     assert oracle.max_abs_err(to_f64(out)[keep], ref[keep]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("nseq", [16, 4])
+def test_merge_workspace_reused_with_new_inputs(pkv, nseq):
+    """Consecutive calls on one workspace of random bytes, each with its own
+    query and cache: every output matches the oracle for its own inputs (no
+    call reads another call's partials or merge counts), and a second round
+    gives the first round's bits.  16 sequences of up to 4096 tokens plan 8
+    splits each, merged inside the launch by the last split; 4 sequences
+    plan 16, merged by the reduce kernel."""
+    lens = [4096, 3000, 4000, 2049] * (nseq // 4)
+    cases = [_case(lens, 12, 2, 128, "bf16", 840 + 10 * nseq + i) for i in range(3)]
+    nws = _ws_bytes(pkv, cases[0][0], 0)
+    assert nws > 0
+    ws = torch.randint(0, 256, (nws,), dtype=torch.uint8, device="cuda")
+    first = []
+    for rnd in range(2):
+        for i, (w, c, gc, q) in enumerate(cases):
+            say(f"reused workspace: {nseq} sequences, round {rnd} case {i}")
+            out = _decode(pkv, w, gc, q, ws, 0)
+            if rnd == 0:
+                ref = oracle.ref_decode(q_exact_values(q), c, w.block_tables, w.context_lens,
+                                        w.scale, w.num_q_heads)
+                assert oracle.max_abs_err(to_f64(out), ref) <= TOL["bf16"]
+                first.append(out)
+            else:
+                assert torch.equal(out, first[i])
