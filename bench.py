@@ -6,8 +6,9 @@ attention shape (batch 64, 12 query / 2 KV heads, head_dim 128, 16-token
 pages, context lengths uniform in [512, 4096], pages scattered over a
 20k-page pool).  One step = the step's 64 new tokens appended + the decode
 over every context, as one fused call (paged_attn_decode_append: the
-split-context partition kernel, which also stores the new tokens, then the
-log-sum-exp reduce kernel on the same stream when a context is split); the
+split-context partition kernel, which also stores the new tokens and, when
+a context is split into at most eight partitions, merges them by their
+log-sum-exps in the same launch; longer plans add the reduce kernel); the
 same step as two calls (append, then decode) is reported beside it.  Before every
 timed step a 1 GiB read evicts L2 and the 256 MB MALL, so every step reads
 its KV from HBM; each step is timed with HIP events on the stream the
@@ -619,7 +620,7 @@ def main():
     for name in ("C3", "C5", "C1", "W1", "F1"):
         if name in only:
             _, r, _ = bench_decode(g, name, args.steps, args.warmup)
-            # the plain decode call (partition + reduce kernels), as profiled
+            # the plain decode call (the partition kernel, with the split merge), as profiled
             r["roofline"] = {"bound": "hbm", "achieved": r["decode_only_call_gbs"], "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": r["decode_only_call_gbs"] / HBM_PEAK_GBS,
                              "traffic": profiled_traffic(f"decode_{name}_counters.txt",
@@ -655,7 +656,7 @@ def main():
             "config": {"workload": DESC["C2"], "batch": 64, "num_q_heads": 12, "num_kv_heads": 2,
                        "head_dim": 128, "page_size": 16, "kv_dtype": "bf16",
                        "context_tokens": int(w2.context_lens.sum()),
-                       "step": "64 new tokens appended + decode, one fused call (partition kernel with the append, then LSE reduce kernel)",
+                       "step": "64 new tokens appended + decode, one fused call (one partition kernel: the append, the attention and the split merge)",
                        "timing": "HIP events per step on the library's stream; 1 GiB read-only flush before each step, outside the events"},
             "hbm_frac": round(head["hbm_frac_step"], 4),
             "seq_tokens_per_s": round(head["seq_tokens_per_s"], 1),
@@ -664,7 +665,7 @@ def main():
                          "frac": round(head["decode_call_gbs"] / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("decode_C2_counters.txt",
                                                      source_sha("decode.hip", "decode_body.h", "pkv_device.h", "pkv_host.h")),
-                         "kernel": "paged_attn_decode_append call: decode_partition_kernel<128,bf16,fused> + decode_reduce_kernel<128>, events around both",
+                         "kernel": "paged_attn_decode_append call: decode_partition_kernel<128,bf16,fused> (the split merge in the same launch), events around the call",
                          "algorithmic_bytes_per_launch": head["effective_kv_bytes"],
                          # the same bytes read by the plain streaming probe:
                          # the practical ceiling, not the published peak
