@@ -81,20 +81,22 @@ def test_large_batch_with_few_split_contexts(pkv):
     assert oracle.max_abs_err(to_f64(out), ref) <= TOL["bf16"]
 
 
-def test_merge_propagates_nan(pkv):
+@pytest.mark.parametrize("nseq", [16, 4])
+def test_merge_propagates_nan(pkv, nseq):
     """A bad page id in one split of a split context makes that sequence's
     rows NaN through the merge; the other sequences keep the oracle's
-    values."""
-    w, c, gc, q = _case([3000, 2900, 2000, 4096], 12, 2, 128, "bf16", 830)
+    values.  16 sequences plan 8 splits each (merged inside the launch), 4
+    plan 16 (the reduce kernel)."""
+    w, c, gc, q = _case([3000, 2900, 2000, 4096] * (nseq // 4), 12, 2, 128, "bf16", 830)
     bt = w.block_tables.copy()
     bt[1, 5] = w.num_pages + 3
     nws = _ws_bytes(pkv, w, 0)
     out = _decode(pkv, w, gc, q, torch.empty(nws, dtype=torch.uint8, device="cuda"), 0,
                   block_tables=bt)
     o = out.cpu().numpy()
-    assert np.all(np.isnan(o[1])) and np.all(np.isfinite(o[[0, 2, 3]]))
+    keep = [i for i in range(nseq) if i != 1]
+    assert np.all(np.isnan(o[1])) and np.all(np.isfinite(o[keep]))
     ref = oracle.ref_decode(q_exact_values(q), c, w.block_tables, w.context_lens, w.scale, 12)
-    keep = [0, 2, 3]
     assert oracle.max_abs_err(to_f64(out)[keep], ref[keep]) <= TOL["bf16"]
 
 
@@ -123,3 +125,21 @@ def test_merge_workspace_reused_with_new_inputs(pkv, nseq):
                 first.append(out)
             else:
                 assert torch.equal(out, first[i])
+
+
+def test_merge_in_launch_two_head_tiles_and_short_contexts(pkv):
+    """16 sequences of a 20-head group (two head tiles per KV head, each
+    with its own arrival counter), 4 splits planned: long contexts merge
+    inside the launch, contexts of one split write their rows directly, and
+    empty contexts give zeros; all match the oracle."""
+    ctx = [4096, 3500, 0, 200, 4000, 1, 2100, 4096, 3000, 64, 2049, 4095, 700, 0, 3900, 1500]
+    w, c, gc, q = _case(ctx, 40, 2, 64, "f16", 860)
+    nws = _ws_bytes(pkv, w, 0)
+    assert nws > 0
+    ws = torch.randint(0, 256, (nws,), dtype=torch.uint8, device="cuda")
+    say("in-launch merge: 16 sequences, hq 40, hkv 2, d 64, f16")
+    out = _decode(pkv, w, gc, q, ws, 0)
+    ref = oracle.ref_decode(q_exact_values(q), c, w.block_tables, w.context_lens, w.scale, 40)
+    assert oracle.max_abs_err(to_f64(out), ref) <= TOL["f16"]
+    again = _decode(pkv, w, gc, q, ws, 0)
+    assert torch.equal(out, again)
