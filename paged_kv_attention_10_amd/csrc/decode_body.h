@@ -433,17 +433,21 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, char*
   float qf[kF32 ? NSTEP : 1];
   H8 qhi[kF32 ? 1 : NSTEP], qlo[kF32 ? 1 : NSTEP];
   float head_c = a.scale_log2;   // scale * log2(e) * 2^-e for this lane's head
+  // columns past the group's heads are zeroed with a mask rather than a
+  // branch per element (which would put a wait and a branch around every
+  // conversion ahead of the first tile loads)
+  const uint32_t q_mask = q_live ? 0xffffffffu : 0u;
   if constexpr (kF32) {
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s)
-      qf[s] = q_live ? io_value_sel(io_word_bits(qw[s >> 2], s & 3, a.q_dtype), a.q_dtype) : 0.f;
+      qf[s] = __uint_as_float(__float_as_uint(io_value_sel(io_word_bits(qw[s >> 2], s & 3, a.q_dtype), a.q_dtype)) & q_mask);
   } else {
     float x[NSTEP][8];
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        x[s][e] = q_live ? io_value_sel(io_word_bits(qw[s], e, a.q_dtype), a.q_dtype) : 0.f;
+        x[s][e] = __uint_as_float(__float_as_uint(io_value_sel(io_word_bits(qw[s], e, a.q_dtype), a.q_dtype)) & q_mask);
     if constexpr (!kBF16) {
       // fp16 operands (fp16, int8 and FP8 caches): the head's query is scaled
       // by the power of two 2^e that puts its largest magnitude in
